@@ -1,0 +1,341 @@
+/*
+ * KDA decode / spec-verify core -- plain sequential CPU oracle.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg load this library. The GPU library shares no code, header,
+ * table or helper with it, and neither side includes or links the other.
+ *
+ * Page abbreviations used in the citations below:
+ *   [kda]      page "vllm.models.kimi_k3.amd.specialized_decode.mono.attention.kda"
+ *              (K1 kda_pre: module docstring with the role table, function list)
+ *   [prepared] page "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.kda.prepared"
+ *              (PreparedKda, decode_conv_weight)
+ *
+ * The pages name the steps and their order ([kda] module docstring, "kda tasks"
+ * row: conv update, f_b MFMA + lower-bound gate, l2norm, the recurrence on
+ * 16-row state chunks with a state written per token, gated RMSNorm ->
+ * core_out) and the operand layout ([prepared] PreparedKda._operands). They
+ * print no formula; the formulas below are the plain readings of those steps.
+ *
+ * Arithmetic: every step is evaluated in IEEE double, in the order written.
+ * Values are rounded only where they are stored: the recurrent state to fp32
+ * (round-to-nearest-even) after every token, core_out to bf16 (RNE), conv
+ * windows copied exactly (they hold bf16 inputs). Carrying the fp32-rounded
+ * state makes a verify call over L tokens equal L chained decode calls bit
+ * for bit.
+ *
+ * Parity status: every step has a pin in the CPU tests (closed forms,
+ * invariants, library routines, brute force). Readings that no printed value
+ * fixes -- the l2norm epsilon, the norm-weight shape, no bf16 rounding
+ * between fused steps -- are the adopted readings, not pinned by the pages.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define KDA_REF_HEAD_DIM 128 /* dk = dv = 128 ([prepared] PreparedKda.__init__: dim = 128 * heads) */
+#define KDA_REF_FA_RANK 128  /* f_a columns ([prepared] _operands: projected[:, 4d : 4d + 128]) */
+
+/* ---------------------------------------------------------------------- */
+/* Number formats                                                          */
+/* ---------------------------------------------------------------------- */
+
+double kda_ref_bf16_to_double(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Direct round-to-nearest-even of a double to bf16 (8 significant bits,
+ * fp32's exponent range, subnormals kept). No intermediate float rounding. */
+uint16_t kda_ref_double_to_bf16(double x)
+{
+    if (isnan(x)) return (uint16_t)0x7fc0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isinf(a)) return (uint16_t)(sign | 0x7f80);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);                       /* a = m * 2^e, m in [0.5, 1) */
+    int qexp = e - 8;                   /* quantum of an 8-bit significand */
+    if (qexp < -133) qexp = -133;       /* bf16 subnormal quantum 2^-133 */
+    double q = ldexp(1.0, qexp);
+    double r = nearbyint(a / q) * q;    /* a / q exact; nearbyint ties to even */
+    const double bf16_max = ldexp(255.0, 120); /* (2 - 2^-7) * 2^127 */
+    if (r > bf16_max) return (uint16_t)(sign | 0x7f80);
+    float f = (float)r;                 /* exact: r has <= 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | ((u >> 16) & 0x7fff));
+}
+
+/* ---------------------------------------------------------------------- */
+/* Step functions (double in, double out)                                  */
+/* ---------------------------------------------------------------------- */
+
+/* Logistic sigmoid, written as 1 / (1 + e^-x) so that large |x| saturates to
+ * 0 or 1 without overflow. */
+double kda_ref_sigmoid(double x)
+{
+    return 1.0 / (1.0 + exp(-x));
+}
+
+/* Causal short-conv update of one token for C channels, then SiLU
+ * ([kda] module docstring, kda tasks: "conv update of the owned channels";
+ * function kda_conv: the spec conv update of a request's L tokens).
+ *
+ * w is the nn.Conv1d weight [C][1][W] read as [C][W] ([prepared]
+ * decode_conv_weight takes the [3 * D, 1, width] weight). nn.Conv1d is a
+ * cross-correlation: with left padding W - 1, tap j multiplies the input
+ * W - 1 - j steps back, so tap W - 1 is the current input x and taps
+ * 0 .. W - 2 the cached window, oldest first.
+ *
+ * win is [C][W - 1], oldest input first; it is shifted in place to hold the
+ * last W - 1 inputs including x. bias may be NULL (no conv bias: zero). */
+void kda_ref_conv_token(int32_t C, int32_t W, const double* w, const double* bias,
+                        double* win, const double* x, double* y)
+{
+    for (int32_t c = 0; c < C; ++c) {
+        const double* wc = w + (int64_t)c * W;
+        double* wn = win + (int64_t)c * (W - 1);
+        double pre = bias ? bias[c] : 0.0;
+        for (int32_t m = 0; m < W - 1; ++m) pre += wc[m] * wn[m];
+        pre += wc[W - 1] * x[c];
+        y[c] = pre * kda_ref_sigmoid(pre);           /* SiLU */
+        for (int32_t m = 0; m + 1 < W - 1; ++m) wn[m] = wn[m + 1];
+        if (W > 1) wn[W - 2] = x[c];
+    }
+}
+
+/* Channel-wise decay gate of one token for all H heads ([kda] kda tasks:
+ * "f_b MFMA + lower-bound gate"; function kda_gates: g1 = f_b f_a).
+ *   g1[i] = sum_m f_b[i][m] * f_a[m]               (f_b is [D][128])
+ *   g[i]  = lb * sigmoid(exp(A_log[i / 128]) * (g1[i] + dt_bias[i]))
+ * A_log has one value per head ([prepared] PreparedKda.__init__: heads =
+ * A_log.numel()); dt_bias has one per channel. */
+void kda_ref_gate(int32_t H, const double* f_b, const double* f_a, const double* A_log,
+                  const double* dt_bias, double lb, double* g)
+{
+    const int32_t D = H * KDA_REF_HEAD_DIM;
+    for (int32_t i = 0; i < D; ++i) {
+        double g1 = 0.0;
+        for (int32_t m = 0; m < KDA_REF_FA_RANK; ++m)
+            g1 += f_b[(int64_t)i * KDA_REF_FA_RANK + m] * f_a[m];
+        double a = exp(A_log[i / KDA_REF_HEAD_DIM]);
+        g[i] = lb * kda_ref_sigmoid(a * (g1 + dt_bias[i]));
+    }
+}
+
+/* l2 normalisation with the epsilon inside the square root, then a scale
+ * ([kda] kda tasks: "l2norm"; the 128^-0.5 q scale is the second of the
+ * scalars in [prepared] PreparedKda.__init__):
+ *   out = x * scale / sqrt(sum x^2 + eps). A zero vector maps to zero. */
+void kda_ref_l2norm(int32_t n, const double* x, double eps, double scale, double* out)
+{
+    double ss = 0.0;
+    for (int32_t i = 0; i < n; ++i) ss += x[i] * x[i];
+    double inv = 1.0 / sqrt(ss + eps);
+    for (int32_t i = 0; i < n; ++i) out[i] = x[i] * inv * scale;
+}
+
+/* One token of the gated delta rule on one head's state ([kda] kda tasks:
+ * "the recurrence on 16 state rows"; function kda_recur: state rows of head
+ * h, the recurrence over the L tokens).
+ *
+ * Storage: S is [dv][dk], row j = value channel j (the pages split the state
+ * into 16-row v-chunks), column i = key channel i. In matrix terms, with
+ * M = S^T ([dk][dv]):  M <- diag(e^g) M;  M <- M + beta k (v - M^T k)^T;
+ * o = M^T q. Row by row, in that order:
+ *   S[j][i] *= exp(g[i])
+ *   u = v[j] - sum_i S[j][i] k[i]
+ *   S[j][i] += (beta * u) * k[i]
+ *   o[j] = sum_i S[j][i] q[i]                                            */
+void kda_ref_recur_token(int32_t dk, int32_t dv, double* S, const double* g, const double* k,
+                         const double* q, const double* v, double beta, double* o)
+{
+    for (int32_t j = 0; j < dv; ++j) {
+        double* row = S + (int64_t)j * dk;
+        for (int32_t i = 0; i < dk; ++i) row[i] *= exp(g[i]);
+        double kS = 0.0;
+        for (int32_t i = 0; i < dk; ++i) kS += row[i] * k[i];
+        double bu = beta * (v[j] - kS);
+        for (int32_t i = 0; i < dk; ++i) row[i] += bu * k[i];
+        double acc = 0.0;
+        for (int32_t i = 0; i < dk; ++i) acc += row[i] * q[i];
+        o[j] = acc;
+    }
+}
+
+/* Head-wise gated RMSNorm of one head's n outputs ([kda] kda tasks: "gated
+ * RMSNorm -> core_out"; function kda_norm: over the head's 128):
+ *   rstd = 1 / sqrt(mean_j o[j]^2 + eps);  y[j] = o[j] * rstd * w[j] * sigmoid(gate[j]) */
+void kda_ref_gated_rmsnorm(int32_t n, const double* o, const double* gate, const double* w,
+                           double eps, double* y)
+{
+    double ss = 0.0;
+    for (int32_t j = 0; j < n; ++j) ss += o[j] * o[j];
+    double rstd = 1.0 / sqrt(ss / (double)n + eps);
+    for (int32_t j = 0; j < n; ++j) y[j] = o[j] * rstd * w[j] * kda_ref_sigmoid(gate[j]);
+}
+
+/* ---------------------------------------------------------------------- */
+/* One decode or verify call                                               */
+/* ---------------------------------------------------------------------- */
+
+typedef struct {
+    int32_t heads;              /* H; head dim 128, D = 128 H */
+    int32_t width;              /* conv taps W (>= 1) */
+    int32_t requests;           /* R */
+    int32_t tokens;             /* L tokens a request; S = R L rows */
+    const uint16_t* projected;  /* bf16 [S][pitch]: q|k|v (3D), gate (D), f_a (128), beta (H) */
+    int64_t pitch;              /* elements */
+    const int32_t* slots;       /* slots[r * slots_row_stride + t] */
+    int64_t slots_row_stride;
+    const int32_t* accepted;    /* [R] in 1..L (verify), or NULL (decode: L == 1) */
+    int32_t num_slots;
+    uint16_t* conv;             /* bf16 conv-window pool, element strides below */
+    int64_t conv_slot_stride, conv_dim_stride, conv_pos_stride;
+    float* state;               /* fp32 [num_slots][slot stride]; [h][v][k] within a slot */
+    int64_t state_slot_stride;
+    const uint16_t* conv_weight;/* bf16 [3D][1][W] (nn.Conv1d layout) */
+    const uint16_t* conv_bias;  /* bf16 [3D], or NULL */
+    const uint16_t* f_b;        /* bf16 [D][128] */
+    const float* A_log;         /* [H] */
+    const float* dt_bias;       /* [D] */
+    const float* norm_weight;   /* [128] shared (stride 0) or [H][128] (stride 128) */
+    int32_t norm_head_stride;
+    double gate_lower_bound;
+    double q_scale;             /* 128^-0.5 */
+    double norm_eps;
+    double l2_eps;
+    uint16_t* core_out;         /* bf16 [S][D] */
+    double* core_out_f64;       /* optional [S][D]: the value before the bf16 rounding */
+} kda_ref_problem;
+
+/* Slot resolution ([prepared] PreparedKda.run and _operands: slots [B] for a
+ * decode step; slots [>= B, q] with accepted [>= B] for a verify step).
+ * Decode: the state is read and written in place at slots[r]. Verify: the
+ * carried state is the one written for the last accepted token of the
+ * previous step, slots[r][accepted[r] - 1]; token t writes slots[r][t].
+ * Returns 0 when every index is in range, else -1 (the request is skipped). */
+static int resolve_slots(const kda_ref_problem* p, int32_t r, int32_t* src, int32_t* dst)
+{
+    const int32_t L = p->tokens;
+    const int32_t* row = p->slots + (int64_t)r * p->slots_row_stride;
+    for (int32_t t = 0; t < L; ++t) {
+        dst[t] = row[t];
+        if (dst[t] < 0 || dst[t] >= p->num_slots) return -1;
+    }
+    if (p->accepted == NULL) {
+        *src = dst[0];
+    } else {
+        int32_t a = p->accepted[r];
+        if (a < 1 || a > L) return -1;
+        *src = row[a - 1];
+    }
+    return 0;
+}
+
+/* Runs one call. The conv and state pools are updated in place; core_out rows
+ * of skipped requests are left untouched. Returns the number of skipped
+ * requests (an index out of range), or -1 on an invalid problem. */
+int32_t kda_ref_run(const kda_ref_problem* p)
+{
+    const int32_t H = p->heads, W = p->width, R = p->requests, L = p->tokens;
+    if (H <= 0 || W < 1 || R < 0 || L < 1 || p->pitch < 0) return -1;
+    if (p->accepted == NULL && L != 1) return -1;
+    const int32_t N = KDA_REF_HEAD_DIM, D = H * N, C = 3 * D;
+    if (p->pitch < 4 * (int64_t)D + KDA_REF_FA_RANK + H) return -1;
+
+    /* Weights in double, nn.Conv1d weight [C][1][W] read as [C][W]. */
+    double* w = malloc(sizeof(double) * (size_t)C * W);
+    double* b = p->conv_bias ? malloc(sizeof(double) * (size_t)C) : NULL;
+    double* fb = malloc(sizeof(double) * (size_t)D * KDA_REF_FA_RANK);
+    double* alog = malloc(sizeof(double) * (size_t)H);
+    double* dtb = malloc(sizeof(double) * (size_t)D);
+    double* nw = malloc(sizeof(double) * (size_t)H * N);
+    double* win = malloc(sizeof(double) * (size_t)C * (W > 1 ? W - 1 : 1));
+    double* S = malloc(sizeof(double) * (size_t)H * N * N);
+    double* x = malloc(sizeof(double) * (size_t)p->pitch);
+    double* y = malloc(sizeof(double) * (size_t)C);
+    double* g = malloc(sizeof(double) * (size_t)D);
+    double* qh = malloc(sizeof(double) * (size_t)N);
+    double* kh = malloc(sizeof(double) * (size_t)N);
+    double* o = malloc(sizeof(double) * (size_t)N);
+    double* gate = malloc(sizeof(double) * (size_t)N);
+    double* yo = malloc(sizeof(double) * (size_t)N);
+    int32_t* dst = malloc(sizeof(int32_t) * (size_t)L);
+    for (int64_t i = 0; i < (int64_t)C * W; ++i) w[i] = kda_ref_bf16_to_double(p->conv_weight[i]);
+    if (b)
+        for (int32_t c = 0; c < C; ++c) b[c] = kda_ref_bf16_to_double(p->conv_bias[c]);
+    for (int64_t i = 0; i < (int64_t)D * KDA_REF_FA_RANK; ++i) fb[i] = kda_ref_bf16_to_double(p->f_b[i]);
+    for (int32_t h = 0; h < H; ++h) alog[h] = (double)p->A_log[h];
+    for (int32_t i = 0; i < D; ++i) dtb[i] = (double)p->dt_bias[i];
+    for (int32_t h = 0; h < H; ++h)
+        for (int32_t j = 0; j < N; ++j)
+            nw[(int64_t)h * N + j] = (double)p->norm_weight[(int64_t)h * p->norm_head_stride + j];
+
+    int32_t skipped = 0;
+    for (int32_t r = 0; r < R; ++r) {
+        int32_t src;
+        if (resolve_slots(p, r, &src, dst) != 0) { ++skipped; continue; }
+
+        /* Read the carried conv window and state before any write. */
+        for (int32_t c = 0; c < C; ++c)
+            for (int32_t m = 0; m < W - 1; ++m)
+                win[(int64_t)c * (W - 1) + m] = kda_ref_bf16_to_double(
+                    p->conv[src * p->conv_slot_stride + c * p->conv_dim_stride + m * p->conv_pos_stride]);
+        for (int64_t e = 0; e < (int64_t)H * N * N; ++e)
+            S[e] = (double)p->state[src * p->state_slot_stride + e];
+
+        for (int32_t t = 0; t < L; ++t) {
+            const int64_t row = (int64_t)r * L + t;
+            const uint16_t* xr = p->projected + row * p->pitch;
+            for (int64_t e = 0; e < p->pitch; ++e) x[e] = kda_ref_bf16_to_double(xr[e]);
+
+            /* conv update + SiLU over q|k|v; the new window goes to dst[t] */
+            kda_ref_conv_token(C, W, w, b, win, x, y);
+            for (int32_t c = 0; c < C; ++c)
+                for (int32_t m = 0; m < W - 1; ++m)
+                    p->conv[dst[t] * p->conv_slot_stride + c * p->conv_dim_stride + m * p->conv_pos_stride] =
+                        kda_ref_double_to_bf16(win[(int64_t)c * (W - 1) + m]);
+
+            /* decay gate from f_a = projected[4D : 4D + 128] */
+            kda_ref_gate(H, fb, x + 4 * (int64_t)D, alog, dtb, p->gate_lower_bound, g);
+
+            for (int32_t h = 0; h < H; ++h) {
+                /* beta = sigmoid(projected[4D + 128 + h]), one per (token, head) */
+                double beta = kda_ref_sigmoid(x[4 * (int64_t)D + KDA_REF_FA_RANK + h]);
+                kda_ref_l2norm(N, y + (int64_t)h * N, p->l2_eps, p->q_scale, qh);
+                kda_ref_l2norm(N, y + D + (int64_t)h * N, p->l2_eps, 1.0, kh);
+                const double* v = y + 2 * (int64_t)D + (int64_t)h * N;
+                double* Sh = S + (int64_t)h * N * N;
+                kda_ref_recur_token(N, N, Sh, g + (int64_t)h * N, kh, qh, v, beta, o);
+
+                /* the state written for this token, rounded to fp32 and carried */
+                float* out_state = p->state + dst[t] * p->state_slot_stride + (int64_t)h * N * N;
+                for (int64_t e = 0; e < (int64_t)N * N; ++e) {
+                    float f = (float)Sh[e];
+                    out_state[e] = f;
+                    Sh[e] = (double)f;
+                }
+
+                /* gated RMSNorm with gate = projected[3D + 128 h + j] */
+                for (int32_t j = 0; j < N; ++j) gate[j] = x[3 * (int64_t)D + (int64_t)h * N + j];
+                kda_ref_gated_rmsnorm(N, o, gate, nw + (int64_t)h * N, p->norm_eps, yo);
+                for (int32_t j = 0; j < N; ++j) {
+                    int64_t oi = row * D + (int64_t)h * N + j;
+                    p->core_out[oi] = kda_ref_double_to_bf16(yo[j]);
+                    if (p->core_out_f64) p->core_out_f64[oi] = yo[j];
+                }
+            }
+        }
+    }
+
+    free(w); free(b); free(fb); free(alog); free(dtb); free(nw); free(win); free(S); free(x);
+    free(y); free(g); free(qh); free(kh); free(o); free(gate); free(yo); free(dst);
+    return skipped;
+}

@@ -1,0 +1,70 @@
+"""Strength of the oracle's pins: copies of the oracle with one planted mistake
+(built on the CPU into a temporary directory) must each fail at least one pin.
+
+Each mutation is a plausible slip in one step: a dropped term, a wrong sign,
+index or operand, a transposed weight, a missing rounding."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from oracle_pins import PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "kda_oracle.c")
+
+MUTATIONS = {
+    "conv_taps_reversed": ("pre += wc[m] * wn[m];", "pre += wc[W - 2 - m] * wn[m];"),
+    "conv_bias_dropped": ("double pre = bias ? bias[c] : 0.0;", "double pre = 0.0;"),
+    "conv_silu_dropped": ("y[c] = pre * kda_ref_sigmoid(pre);", "y[c] = pre;"),
+    "conv_window_not_shifted": ("if (W > 1) wn[W - 2] = x[c];", ";"),
+    "gate_dt_bias_dropped": ("(g1 + dt_bias[i])", "(g1)"),
+    "gate_a_log_head_index": ("exp(A_log[i / KDA_REF_HEAD_DIM])", "exp(A_log[0])"),
+    "gate_f_b_transposed": ("f_b[(int64_t)i * KDA_REF_FA_RANK + m]",
+                            "f_b[(int64_t)m * KDA_REF_FA_RANK + i % KDA_REF_FA_RANK]"),
+    "gate_no_exp_on_a_log": ("double a = exp(A_log[i / KDA_REF_HEAD_DIM]);",
+                             "double a = A_log[i / KDA_REF_HEAD_DIM];"),
+    "sigmoid_sign": ("return 1.0 / (1.0 + exp(-x));", "return 1.0 / (1.0 + exp(x));"),
+    "l2norm_eps_outside_sqrt": ("double inv = 1.0 / sqrt(ss + eps);",
+                                "double inv = 1.0 / (sqrt(ss) + eps);"),
+    "recur_decay_by_row": ("row[i] *= exp(g[i]);", "row[i] *= exp(g[j % dk]);"),
+    "recur_u_sign": ("double bu = beta * (v[j] - kS);", "double bu = beta * (v[j] + kS);"),
+    "recur_update_uses_q": ("row[i] += bu * k[i];", "row[i] += bu * q[i];"),
+    "recur_beta_dropped": ("double bu = beta * (v[j] - kS);", "double bu = (v[j] - kS);"),
+    "rmsnorm_sum_not_mean": ("double rstd = 1.0 / sqrt(ss / (double)n + eps);",
+                             "double rstd = 1.0 / sqrt(ss + eps);"),
+    "rmsnorm_gate_dropped": ("y[j] = o[j] * rstd * w[j] * kda_ref_sigmoid(gate[j]);",
+                             "y[j] = o[j] * rstd * w[j];"),
+    "verify_reads_first_slot": ("*src = row[a - 1];", "*src = row[0];"),
+    "state_not_carried_rounded": ("Sh[e] = (double)f;", ";"),
+    "conv_window_written_reversed": (
+        "p->conv[dst[t] * p->conv_slot_stride + c * p->conv_dim_stride + m * p->conv_pos_stride] =",
+        "p->conv[dst[t] * p->conv_slot_stride + c * p->conv_dim_stride + (W - 2 - m) * p->conv_pos_stride] ="),
+    "beta_head_index": ("x[4 * (int64_t)D + KDA_REF_FA_RANK + h]", "x[4 * (int64_t)D + KDA_REF_FA_RANK]"),
+    "q_scale_on_k": ("kda_ref_l2norm(N, y + D + (int64_t)h * N, p->l2_eps, 1.0, kh);",
+                     "kda_ref_l2norm(N, y + D + (int64_t)h * N, p->l2_eps, p->q_scale, kh);"),
+    "bf16_truncates": ("double r = nearbyint(a / q) * q;", "double r = floor(a / q) * q;"),
+    "gate_reads_gate_columns": ("kda_ref_gate(H, fb, x + 4 * (int64_t)D,",
+                                "kda_ref_gate(H, fb, x + 3 * (int64_t)D,"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique in the oracle: {old!r}"
+    mutated = tmp_path / "kda_oracle_mutant.c"
+    mutated.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
+                    "-o", str(lib), str(mutated), "-lm"], check=True)
+    orc = oracle.Oracle(str(lib))
+    caught = []
+    for check in PINS:
+        try:
+            check(orc)
+        except (AssertionError, ValueError):
+            caught.append(check.__name__)
+            break
+    assert caught, f"no pin catches the planted mistake {name}"
