@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Throughput of the KDA spec-verify core on one MI355X (gfx950).
+
+One step is one kda_verify call over the whole batch: for R x L rows and 12
+heads it runs the conv update, the decay gate (MFMA), beta, l2norm, the gated
+delta rule with a state written per token, and the gated RMSNorm. Inputs are
+seeded synthetic tensors at the pages' shapes (12 heads x 128 channels per
+tensor-parallel rank, f_a rank 128, width-4 conv), resident in HBM before the
+timed region starts.
+
+The default workload is the large spec-verify batch: R = 64 requests x L = 8
+tokens (S = 512 rows), a pool of 1024 slots addressed through a [64, 16] block
+table, accepted counts ~ U{1..8}. Successive steps alternate between the two
+8-column halves of the block table, so that a step's reads come from slots
+written two steps earlier, with ~420 MB of other writes in between: the 256 MB
+Infinity Cache cannot hold them, and the rate is the HBM rate.
+
+Metric bytes per step (state + conv window, read once per request and written
+once per token): (R + S) x H x 67,840 B, where a unit of 67,840 B is one
+128 x 128 fp32 state tile plus one 3 x 384 bf16 conv window.
+
+Prints one JSON line. `--config N` selects another workload (0..4) for
+exploration; `--probe` adds the plain read / write / copy HBM probes.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA verify tokens/s and achieved HBM GB/s (state+conv R/W) at R x L"
+UNIT_BYTES = 128 * 128 * 4 + 3 * 128 * 3 * 2        # state tile + conv window of one head
+HBM_PEAK_GBPS = 8000.0                                # MI355X published HBM3E bandwidth
+KERNEL_NAME = "kda_core_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_core_traffic.json")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3, help="workload 0..4 (default 3)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall-clock budget of the oracle baseline (0 disables it)")
+    ap.add_argument("--probe", action="store_true", help="also run the HBM probes")
+    ap.add_argument("--probe-only", action="store_true",
+                    help="run only the HBM probes (counter calibration)")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    import hashlib
+    path = os.path.join(ROOT, "kimi_delta_attention_conv_amd", "csrc", "kda_core.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def rotation_sets(case, torch):
+    """Disjoint slot sets of the pool, each laid out like case.slots.
+
+    Returns (flat int32 base, [(shape, stride, offset)]): every set is a view of
+    the base, so a block-table slice keeps its row stride on the device."""
+    S, L = case.S, case.L
+    if case.slots.dim() == 2 and case.slots.stride(0) > L:
+        cols = case.slots.stride(0)
+        base = torch.as_strided(case.slots, (case.R * cols,), (1,), case.slots.storage_offset())
+        views = [((case.R, L), (cols, 1), j * L) for j in range(cols // L)]
+        return base.contiguous(), views
+    first = case.slots.reshape(-1)
+    used = set(first.tolist())
+    perm = torch.randperm(case.num_slots, generator=torch.Generator().manual_seed(77)).tolist()
+    rest = [x for x in perm if x not in used]
+    chunks = [first]
+    while len(rest) >= S:
+        chunks.append(torch.tensor(rest[:S], dtype=torch.int32))
+        rest = rest[S:]
+    shape, stride = tuple(case.slots.shape), tuple(case.slots.contiguous().stride())
+    views = [(shape, stride, k * S) for k in range(len(chunks))]
+    return torch.cat(chunks).contiguous(), views
+
+
+def probe(torch, kda):
+    """Achievable HBM GB/s of plain read, write and copy streams (1 GiB buffers)."""
+    lib = kda.load_library()
+    nbytes = 1 << 30
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    sink = torch.empty(lib.kda_probe_sink_floats(), dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    calls = {
+        "read": lambda: lib.kda_probe_read(a.data_ptr(), nbytes, sink.data_ptr(), s),
+        "write": lambda: lib.kda_probe_write(b.data_ptr(), nbytes, 2.0, s),
+        "copy": lambda: lib.kda_probe_copy(b.data_ptr(), a.data_ptr(), nbytes, s),
+    }
+    moved = {"read": nbytes, "write": nbytes, "copy": 2 * nbytes}
+    res = {}
+    for name, fn in calls.items():
+        for _ in range(3):
+            assert fn() == 0
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 10
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        res[name] = dict(gbps=round(moved[name] / (ms * 1e-3) / 1e9, 1), ms=round(ms, 4),
+                         bytes=moved[name])
+    del a, b, sink
+    return res
+
+
+def cpu_baseline(case, seconds):
+    """The oracle, as it stands, timed on the host on the same workload."""
+    import numpy as np
+
+    import oracle
+    orc = oracle.default()
+
+    def u16(t):
+        return t.detach().contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+
+    conv = u16(case.conv_storage).copy()
+    state = case.state.numpy().copy()
+    out = np.zeros((case.S, case.D), np.uint16)
+    s = case.slots
+    span = (s.shape[0] - 1) * s.stride(0) + s.shape[1] if s.dim() == 2 else s.numel()
+    flat = __import__("torch").as_strided(s, (span,), (1,), s.storage_offset()).contiguous().numpy()
+    kw = dict(heads=case.H, width=case.W, requests=case.R, tokens=case.L,
+              projected=u16(case.projected), pitch=case.pitch, slots=flat,
+              slots_row_stride=case.slots_row_stride(),
+              accepted=None if case.accepted is None else case.accepted.numpy(),
+              num_slots=case.num_slots, conv=conv.reshape(-1), conv_strides=case.conv_strides(),
+              state=state.reshape(-1), state_slot_stride=case.H * 128 * 128,
+              conv_weight=u16(case.conv_weight),
+              conv_bias=None if case.conv_bias is None else u16(case.conv_bias),
+              f_b=u16(case.f_b), A_log=case.A_log.numpy(), dt_bias=case.dt_bias.numpy(),
+              norm_weight=case.norm_weight.numpy(), norm_head_stride=0,
+              gate_lower_bound=case.gate_lower_bound, norm_eps=case.norm_eps,
+              l2_eps=case.l2_eps, core_out=out)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.run(**kw)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return dict(value=round(case.S * reps / el, 2), unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{reps} full calls of the same workload ({case.R} requests x {case.L} "
+                       f"tokens x {case.H} heads), single-threaded C oracle in double, "
+                       f"{el:.1f} s")
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the core shards by heads and requests with no exchange; multi-GPU runs are "
+              "out of scope)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kimi_delta_attention_conv_amd as kda
+    from kda_inputs import make_config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    if args.probe_only:
+        print(json.dumps({"hbm_probe": probe(torch, kda)}), flush=True)
+        return
+
+    case = make_config(args.config)
+    dev = "cuda"
+    conv_storage = case.conv_storage.to(dev)
+    conv = conv_storage if case.conv_dim_first else conv_storage.transpose(-1, -2)
+    state = case.state.to(dev)
+    core = kda.KdaCore(conv_weight=case.conv_weight.to(dev),
+                       conv_bias=None if case.conv_bias is None else case.conv_bias.to(dev),
+                       f_b=case.f_b.to(dev), A_log=case.A_log.to(dev),
+                       dt_bias=case.dt_bias.to(dev), norm_weight=case.norm_weight.to(dev),
+                       gate_lower_bound=case.gate_lower_bound, norm_eps=case.norm_eps,
+                       l2_eps=case.l2_eps, conv=conv, state=state)
+    projected = case.projected.to(dev)
+    out = torch.empty(case.S, case.D, dtype=torch.bfloat16, device=dev)
+    slot_base, views = rotation_sets(case, torch)
+    slot_base = slot_base.to(dev)
+    sets = [torch.as_strided(slot_base, shape, stride, off) for shape, stride, off in views]
+    accepted = None if case.accepted is None else case.accepted.to(dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    h = core.handle
+    pitch = case.pitch
+    lib = kda.load_library()
+    if accepted is None:
+        launches = [(lambda s=s: lib.kda_decode(h, projected.data_ptr(), pitch, case.R,
+                                                s.data_ptr(), out.data_ptr(), sp)) for s in sets]
+    else:
+        launches = [(lambda s=s: lib.kda_verify(h, projected.data_ptr(), pitch, case.R, case.L,
+                                                s.data_ptr(), s.stride(0), accepted.data_ptr(),
+                                                out.data_ptr(), sp)) for s in sets]
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        rc = launches[i % len(launches)]()
+        if rc != 0:
+            raise RuntimeError(f"launch failed: {kda.kda_status_string(rc)}")
+    torch.cuda.synchronize()
+    print(f"[bench] {case.name}: warmup {args.warmup} done, timing {args.steps} steps",
+          file=sys.stderr, flush=True)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        launches[(args.warmup + i) % len(launches)]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    errors = core.device_errors()
+    if errors:
+        raise RuntimeError(f"{errors} requests were skipped for invalid slots")
+
+    ms_per_step = wall * 1e3 / args.steps
+    kernel_ms = gpu_ms / args.steps          # one launch of the core kernel per step
+    metric_bytes = (case.R + case.S) * case.H * UNIT_BYTES
+    achieved = metric_bytes / (kernel_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE)).get(case.name)
+        if rec and rec.get("source_digest") == source_digest():
+            traffic = rec.get("bytes_per_launch")
+    result = {
+        "metric": METRIC,
+        "value": round(case.S / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": case.name, "requests": case.R, "tokens": case.L,
+                   "rows": case.S, "heads": case.H, "head_dim": 128, "pool_slots": case.num_slots,
+                   "conv_layout": "dim_first" if case.conv_dim_first else "transposed",
+                   "slot_sets_rotated": len(sets), "io": "bf16", "state": "f32"},
+        "gbps": round(metric_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "metric_bytes_per_step": metric_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": KERNEL_NAME,
+                     "kernel_ms": round(kernel_ms, 5)},
+    }
+    if args.probe:
+        result["hbm_probe"] = probe(torch, kda)
+    core.close()
+    del state, conv_storage
+    torch.cuda.empty_cache()
+    if args.cpu_seconds > 0:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

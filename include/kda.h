@@ -1,0 +1,183 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) KDA decode / spec-verify core.
+ *
+ * One call runs, for R requests x L tokens (S = R L rows) and H heads of 128
+ * channels, the core of a Kimi Delta Attention layer between the packed input
+ * projection and the gated core output:
+ *   1. the causal width-4 conv update with SiLU of the packed q|k|v channels
+ *      against a per-slot conv window cache;
+ *   2. the channel-wise decay gate g = lb * sigmoid(exp(A_log_h) *
+ *      (f_b f_a + dt_bias)) and beta = sigmoid(beta_raw);
+ *   3. l2-normalised q and k, q scaled by 128^-0.5;
+ *   4. the gated delta rule on a 128 x 128 fp32 state per (slot, head):
+ *      S <- diag(e^g) S;  S <- S + beta k (v - S^T k)^T;  o = S^T q,
+ *      with a state written for every token;
+ *   5. the head-wise gated RMSNorm o_norm(o) * sigmoid(gate) into bf16.
+ *
+ * Sources (page titles; sections named, no line numbers):
+ *   [kda]      "vllm.models.kimi_k3.amd.specialized_decode.mono.attention.kda":
+ *              module docstring (K1 kda_pre, "kda tasks" row: conv update,
+ *              f_b MFMA + lower-bound gate, l2norm, the recurrence on 16 state
+ *              rows with a state written per token, gated RMSNorm -> core_out)
+ *              and the host launcher entry kda_pre (conv_state
+ *              [slots, dim, state_len] or a transposed view).
+ *   [prepared] "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.kda.prepared":
+ *              PreparedKda.__init__ (weights, fp32 norm weight, the scalars
+ *              gate_lower_bound, 128^-0.5, o_norm.eps), _operands (the packed
+ *              projection row and the operand set), prepare_caches and run
+ *              (decode: slots [B]; verify: slots [>= B, q], accepted [>= B]),
+ *              decode_conv_weight ([3D, 1, W] -> [3, W, D]).
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are HIP device pointers on the device that is
+ *     current when kda_prepare runs; every later call must use that device.
+ *   - Sizes and strides are in elements unless a name says bytes.
+ *   - Calls are asynchronous and stream ordered: they enqueue work on
+ *     `hip_stream` (a hipStream_t, NULL = the null stream) and return.
+ *   - Every argument is validated on the host before any HIP call. On a
+ *     non-KDA_OK status nothing was enqueued and no device memory changed,
+ *     except for KDA_ERR_HIP (a HIP call failed; see kda_last_hip_error).
+ *   - Nothing unwinds across the ABI; no function allocates on the host per
+ *     call. Only kda_prepare allocates device memory; kda_destroy frees it.
+ *   - Within one call the destination slots of all requests must be distinct
+ *     (a precondition, not checked): overlapping destinations race.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_HEAD_DIM 128   /* dk = dv = 128 ([prepared] PreparedKda.__init__: dim = 128 * heads) */
+#define KDA_FA_RANK 128    /* f_a width ([prepared] _operands: projected[:, 4D : 4D + 128]) */
+#define KDA_CONV_WIDTH 4   /* the only supported conv width W (conv state holds W - 1 = 3 inputs) */
+#define KDA_MAX_TOKENS 8   /* largest verify length L */
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = -1,        /* a required pointer is NULL */
+    KDA_ERR_SHAPE = -2,       /* a count, size, pitch or stride is out of range */
+    KDA_ERR_ALIGN = -3,       /* a pointer, pitch or stride breaks the alignment rules */
+    KDA_ERR_UNSUPPORTED = -4, /* valid but not supported: conv width != 4, L > 8 */
+    KDA_ERR_HIP = -5,         /* a HIP runtime call failed (kda_last_hip_error names it) */
+    KDA_ERR_NOMEM = -6        /* device or host allocation failed in kda_prepare */
+} kda_status;
+
+typedef struct kda_handle_s* kda_handle;
+
+/* Attention weights of one layer ([prepared] PreparedKda.__init__). Borrowed
+ * only during kda_prepare: the library copies and re-lays them out into its
+ * own device memory on `hip_stream`; the caller may free them once that
+ * stream has passed the kda_prepare call. All pointers are device pointers. */
+typedef struct {
+    int32_t heads;            /* H >= 1 heads of 128 channels; D = 128 H */
+    int32_t conv_width;       /* W; must be KDA_CONV_WIDTH */
+    const void* conv_weight;  /* bf16 [3D][1][W], the nn.Conv1d layout (q, k, v channel
+                                 blocks of D); re-laid as [3][W][D] fp32
+                                 ([prepared] decode_conv_weight). 2-byte aligned. */
+    const void* conv_bias;    /* bf16 [3D], or NULL for no conv bias (taken as zero) */
+    const void* f_b;          /* bf16 [D][128], row i = output channel i. 2-byte aligned. */
+    const float* A_log;       /* fp32 [H], one per head ([prepared]: heads = A_log.numel()) */
+    const float* dt_bias;     /* fp32 [D] */
+    const float* norm_weight; /* fp32 o_norm weight: [128] shared by all heads
+                                 (norm_head_stride 0) or [H][128] (stride 128) */
+    int32_t norm_head_stride; /* 0 or 128 */
+    float gate_lower_bound;   /* lb (e.g. -5); finite */
+    float norm_eps;           /* o_norm.eps (e.g. 1e-6); >= 0 */
+    float l2_eps;             /* epsilon inside the l2norm square root (1e-6); >= 0 */
+} kda_weights;
+
+/* The per-slot caches of one layer ([kda] kda_pre launcher: conv_state
+ * [slots, dim, state_len] or a transposed view; [prepared] prepare_caches).
+ * Borrowed for the handle's lifetime: the library records the pointers and
+ * strides; the caller keeps the memory alive and changes it only through
+ * these calls (or between calls, stream ordered).
+ *
+ *   conv  : bf16 windows of the last W - 1 = 3 q|k|v inputs, oldest first.
+ *           Element (slot, channel c < 3D, position m < 3) lives at
+ *           conv + slot * conv_slot_stride + c * conv_dim_stride + m * conv_pos_stride.
+ *           Dim first [slots][3D][3]: strides (9D, 3, 1). Transposed view of
+ *           storage [slots][3][3D]: strides (9D, 1, 3D). Any non-negative
+ *           strides are accepted; those two are the fast paths.
+ *   state : fp32 [slots][H][128 v][128 k] per slot, slot stride
+ *           state_slot_stride >= H * 128 * 128; row v of a head is
+ *           contiguous over k. Base 16-byte aligned, stride a multiple of 4. */
+typedef struct {
+    void* conv;
+    int64_t conv_slot_stride;
+    int64_t conv_dim_stride;
+    int64_t conv_pos_stride;
+    float* state;
+    int64_t state_slot_stride;
+    int32_t num_slots;        /* >= 1; valid slot indices are 0 .. num_slots - 1 */
+} kda_caches;
+
+/* Creates a handle: validates, allocates the handle's device memory, re-lays
+ * the weights out on `hip_stream` ([prepared] PreparedKda.__init__ and
+ * decode_conv_weight) and records the caches. *out is set only on KDA_OK.
+ * Errors: KDA_ERR_NULL (w, c, out, a weight or cache pointer), KDA_ERR_SHAPE
+ * (heads < 1, num_slots < 1, a stride too small or negative, norm_head_stride
+ * not 0 or 128, a non-finite scalar or negative epsilon), KDA_ERR_ALIGN
+ * (state base or stride), KDA_ERR_UNSUPPORTED (conv_width != 4),
+ * KDA_ERR_NOMEM, KDA_ERR_HIP. */
+kda_status kda_prepare(const kda_weights* w, const kda_caches* c, void* hip_stream,
+                       kda_handle* out);
+
+/* One decode step of `batch` requests, one token each ([prepared] run with
+ * slots [B] and no accepted counts). Request b reads and writes its state and
+ * conv window in place at slot slots[b].
+ *   projected : device bf16 [batch][pitch], row b = q|k|v (3D) | gate (D) |
+ *               f_a (128) | beta_raw (H) | padding ([prepared] _operands).
+ *               pitch >= 4D + 128 + H and even; base 4-byte aligned.
+ *   slots     : device int32 [batch].
+ *   core_out  : device bf16 [batch][D]; base 4-byte aligned.
+ * A request whose slot is outside 0 .. num_slots - 1 is skipped entirely (no
+ * read, no write, its core_out row untouched) and counted in the device error
+ * counter (kda_device_errors). batch == 0 is a no-op.
+ * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE (batch < 0, pitch too small or odd),
+ * KDA_ERR_ALIGN, KDA_ERR_HIP. */
+kda_status kda_decode(kda_handle h, const void* projected, int64_t pitch, int32_t batch,
+                      const int32_t* slots, void* core_out, void* hip_stream);
+
+/* One speculative-verify step of `requests` x `tokens` rows ([prepared] run
+ * with slots [>= B, q] and accepted [>= B]; [kda] kda tasks: a state written
+ * per token). Row r L + t of `projected` / `core_out` is token t of request r.
+ *   slots     : device int32; token t of request r writes its state and conv
+ *               window to slot slots[r * slots_row_stride + t]
+ *               (slots_row_stride >= tokens, so a block-table slice passes
+ *               without a copy).
+ *   accepted  : device int32 [requests], each in 1 .. tokens: the carried state
+ *               and window are read from slot slots[r * slots_row_stride +
+ *               accepted[r] - 1], the one written for the last accepted token
+ *               of the previous step.
+ * Other arguments as kda_decode. tokens in 1 .. KDA_MAX_TOKENS. Invalid slot or
+ * accepted values skip the request as in kda_decode. requests == 0 is a no-op.
+ * Errors: as kda_decode, plus KDA_ERR_UNSUPPORTED (tokens > 8) and
+ * KDA_ERR_SHAPE (tokens < 1, slots_row_stride < tokens). */
+kda_status kda_verify(kda_handle h, const void* projected, int64_t pitch, int32_t requests,
+                      int32_t tokens, const int32_t* slots, int64_t slots_row_stride,
+                      const int32_t* accepted, void* core_out, void* hip_stream);
+
+/* Number of requests skipped for an out-of-range slot or accepted count since
+ * the last read. Waits for `hip_stream`, copies the counter to *count_out and
+ * resets it to zero. Errors: KDA_ERR_NULL, KDA_ERR_HIP. */
+kda_status kda_device_errors(kda_handle h, int32_t* count_out, void* hip_stream);
+
+/* Frees the handle and its device memory (after waiting for the device).
+ * NULL is a no-op. The borrowed caches are not touched. */
+kda_status kda_destroy(kda_handle h);
+
+/* Static description of a status code. */
+const char* kda_status_string(kda_status s);
+
+/* The HIP error string of the last KDA_ERR_HIP on this thread, or "". */
+const char* kda_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -100,8 +100,10 @@ CONFIGS = {
 
 
 def default_pitch(H: int) -> int:
+    """4D + 128 + H elements, rounded up to even (the ABI takes 4-byte rows)."""
     D = H * HEAD_DIM
-    return 4 * D + FA_RANK + H
+    p = 4 * D + FA_RANK + H
+    return p + (p & 1)
 
 
 def make_case(R: int, L: int, H: int, num_slots: int, seed: int, *, name: str = "custom",

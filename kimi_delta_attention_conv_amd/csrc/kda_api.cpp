@@ -1,0 +1,249 @@
+// Host side of the C ABI declared in include/kda.h: argument validation (all
+// of it before any HIP call), the handle and its device memory, and the
+// stream-ordered launches of the gfx950 kernels.
+//
+// The call shapes follow page
+// "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.kda.prepared":
+// PreparedKda.__init__ / prepare_caches (kda_prepare) and PreparedKda.run
+// (kda_decode: slots [B]; kda_verify: slots [>= B, q] and accepted [>= B]).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+struct kda_handle_s {
+    int device = 0;
+    int32_t heads = 0;
+    void* dev_mem = nullptr;
+    kda::PreparedWeights w{};
+    int32_t* err_count = nullptr;
+    kda_caches caches{};
+    float lb = 0.0f, norm_eps = 0.0f, l2_eps = 0.0f;
+};
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+kda_status hip_fail(hipError_t e, const char* what) {
+    std::snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s: %s (%d)", what,
+                  hipGetErrorString(e), (int)e);
+    return KDA_ERR_HIP;
+}
+
+constexpr int64_t kAlign = 256;
+
+int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+kda_status check_call(const kda_handle_s* h, const void* projected, int64_t pitch,
+                      int32_t requests, const int32_t* slots, const void* core_out) {
+    if (h == nullptr) return KDA_ERR_NULL;
+    if (requests < 0) return KDA_ERR_SHAPE;
+    if (requests == 0) return KDA_OK;
+    if (projected == nullptr || slots == nullptr || core_out == nullptr) return KDA_ERR_NULL;
+    const int64_t D = (int64_t)h->heads * kda::kHeadDim;
+    if (pitch < 4 * D + kda::kFaRank + h->heads) return KDA_ERR_SHAPE;
+    if (pitch % 2 != 0) return KDA_ERR_SHAPE;
+    if (!aligned(projected, 4) || !aligned(core_out, 4) || !aligned(slots, 4)) return KDA_ERR_ALIGN;
+    // the grid is requests x heads workgroups
+    if ((int64_t)requests * h->heads > INT32_MAX) return KDA_ERR_SHAPE;
+    return KDA_OK;
+}
+
+kda::CoreParams core_params(const kda_handle_s* h, const void* projected, int64_t pitch,
+                            int32_t requests, const int32_t* slots, int64_t slots_row_stride,
+                            const int32_t* accepted, void* core_out) {
+    kda::CoreParams p{};
+    p.projected = static_cast<const uint16_t*>(projected);
+    p.pitch = pitch;
+    p.slots = slots;
+    p.slots_row_stride = slots_row_stride;
+    p.accepted = accepted;
+    p.conv = static_cast<uint16_t*>(h->caches.conv);
+    p.conv_slot_stride = h->caches.conv_slot_stride;
+    p.conv_dim_stride = h->caches.conv_dim_stride;
+    p.conv_pos_stride = h->caches.conv_pos_stride;
+    p.state = h->caches.state;
+    p.state_slot_stride = h->caches.state_slot_stride;
+    p.conv_w = h->w.conv_w;
+    p.conv_b = h->w.conv_b;
+    p.f_b = h->w.f_b;
+    p.a_exp = h->w.a_exp;
+    p.dt_bias = h->w.dt_bias;
+    p.norm_w = h->w.norm_w;
+    p.out = static_cast<uint16_t*>(core_out);
+    p.err_count = h->err_count;
+    p.heads = h->heads;
+    p.requests = requests;
+    p.num_slots = h->caches.num_slots;
+    p.lb = h->lb;
+    p.q_scale = 1.0f / std::sqrt((float)kda::kHeadDim);
+    p.norm_eps = h->norm_eps;
+    p.l2_eps = h->l2_eps;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL: return "a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "a count, size, pitch or stride is out of range";
+        case KDA_ERR_ALIGN: return "a pointer, pitch or stride is misaligned";
+        case KDA_ERR_UNSUPPORTED: return "unsupported configuration (conv width must be 4, tokens <= 8)";
+        case KDA_ERR_HIP: return "a HIP runtime call failed";
+        case KDA_ERR_NOMEM: return "out of memory";
+    }
+    return "unknown status";
+}
+
+const char* kda_last_hip_error(void) { return g_last_hip_error; }
+
+kda_status kda_prepare(const kda_weights* w, const kda_caches* c, void* hip_stream,
+                       kda_handle* out) {
+    if (w == nullptr || c == nullptr || out == nullptr) return KDA_ERR_NULL;
+    if (w->conv_weight == nullptr || w->f_b == nullptr || w->A_log == nullptr ||
+        w->dt_bias == nullptr || w->norm_weight == nullptr || c->conv == nullptr ||
+        c->state == nullptr)
+        return KDA_ERR_NULL;
+    if (w->heads < 1 || w->heads > 4096) return KDA_ERR_SHAPE;
+    if (w->conv_width != kda::kWidth) return KDA_ERR_UNSUPPORTED;
+    if (w->norm_head_stride != 0 && w->norm_head_stride != kda::kHeadDim) return KDA_ERR_SHAPE;
+    if (!std::isfinite(w->gate_lower_bound) || !std::isfinite(w->norm_eps) ||
+        !std::isfinite(w->l2_eps) || w->norm_eps < 0.0f || w->l2_eps < 0.0f)
+        return KDA_ERR_SHAPE;
+    const int64_t H = w->heads, D = H * kda::kHeadDim, C = 3 * D;
+    if (c->num_slots < 1) return KDA_ERR_SHAPE;
+    if (c->conv_slot_stride < 0 || c->conv_dim_stride < 0 || c->conv_pos_stride < 0)
+        return KDA_ERR_SHAPE;
+    // every (channel, position) of a slot must be addressable without overlap in
+    // at least the channel-major sense: the slot stride spans the window block
+    if (c->conv_slot_stride < (C - 1) * c->conv_dim_stride + (kda::kWidth - 2) * c->conv_pos_stride + 1)
+        return KDA_ERR_SHAPE;
+    if (c->state_slot_stride < H * kda::kHeadDim * kda::kHeadDim) return KDA_ERR_SHAPE;
+    if (c->state_slot_stride % 4 != 0 || !aligned(c->state, 16)) return KDA_ERR_ALIGN;
+    if (!aligned(c->conv, 2) || !aligned(w->conv_weight, 2) || !aligned(w->f_b, 2) ||
+        (w->conv_bias != nullptr && !aligned(w->conv_bias, 2)) || !aligned(w->A_log, 4) ||
+        !aligned(w->dt_bias, 4) || !aligned(w->norm_weight, 4))
+        return KDA_ERR_ALIGN;
+
+    kda_handle_s* h = new (std::nothrow) kda_handle_s();
+    if (h == nullptr) return KDA_ERR_NOMEM;
+    hipError_t e = hipGetDevice(&h->device);
+    if (e != hipSuccess) {
+        delete h;
+        return hip_fail(e, "hipGetDevice");
+    }
+    const int64_t b_conv_w = align_up(C * kda::kWidth * 4), b_conv_b = align_up(C * 4),
+                  b_fb = align_up(D * kda::kFaRank * 2), b_a = align_up(H * 4),
+                  b_dt = align_up(D * 4), b_nw = align_up(H * kda::kHeadDim * 4),
+                  b_err = kAlign;
+    const int64_t total = b_conv_w + b_conv_b + b_fb + b_a + b_dt + b_nw + b_err;
+    e = hipMalloc(&h->dev_mem, (size_t)total);
+    if (e != hipSuccess) {
+        delete h;
+        return e == hipErrorOutOfMemory ? KDA_ERR_NOMEM : hip_fail(e, "hipMalloc");
+    }
+    char* base = static_cast<char*>(h->dev_mem);
+    h->w.conv_w = reinterpret_cast<float*>(base);
+    base += b_conv_w;
+    h->w.conv_b = reinterpret_cast<float*>(base);
+    base += b_conv_b;
+    h->w.f_b = reinterpret_cast<uint16_t*>(base);
+    base += b_fb;
+    h->w.a_exp = reinterpret_cast<float*>(base);
+    base += b_a;
+    h->w.dt_bias = reinterpret_cast<float*>(base);
+    base += b_dt;
+    h->w.norm_w = reinterpret_cast<float*>(base);
+    base += b_nw;
+    h->err_count = reinterpret_cast<int32_t*>(base);
+    h->heads = w->heads;
+    h->caches = *c;
+    h->lb = w->gate_lower_bound;
+    h->norm_eps = w->norm_eps;
+    h->l2_eps = w->l2_eps;
+
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    kda::PrepareParams in{};
+    in.conv_weight = static_cast<const uint16_t*>(w->conv_weight);
+    in.conv_bias = static_cast<const uint16_t*>(w->conv_bias);
+    in.f_b = static_cast<const uint16_t*>(w->f_b);
+    in.A_log = w->A_log;
+    in.dt_bias = w->dt_bias;
+    in.norm_weight = w->norm_weight;
+    in.norm_head_stride = w->norm_head_stride;
+    in.heads = w->heads;
+    e = hipMemsetAsync(h->err_count, 0, sizeof(int32_t), s);
+    if (e == hipSuccess) e = kda::launch_prepare(in, h->w, s);
+    if (e != hipSuccess) {
+        kda_status st = hip_fail(e, "prepare launch");
+        (void)hipFree(h->dev_mem);
+        delete h;
+        return st;
+    }
+    *out = h;
+    return KDA_OK;
+}
+
+kda_status kda_decode(kda_handle h, const void* projected, int64_t pitch, int32_t batch,
+                      const int32_t* slots, void* core_out, void* hip_stream) {
+    kda_status st = check_call(h, projected, pitch, batch, slots, core_out);
+    if (st != KDA_OK || batch == 0) return st;
+    const kda::CoreParams p = core_params(h, projected, pitch, batch, slots, 1, nullptr, core_out);
+    hipError_t e = kda::launch_core(1, p, static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? KDA_OK : hip_fail(e, "kda_decode launch");
+}
+
+kda_status kda_verify(kda_handle h, const void* projected, int64_t pitch, int32_t requests,
+                      int32_t tokens, const int32_t* slots, int64_t slots_row_stride,
+                      const int32_t* accepted, void* core_out, void* hip_stream) {
+    if (h == nullptr) return KDA_ERR_NULL;
+    if (tokens < 1) return KDA_ERR_SHAPE;
+    if (tokens > kda::kMaxTokens) return KDA_ERR_UNSUPPORTED;
+    if (slots_row_stride < tokens) return KDA_ERR_SHAPE;
+    kda_status st = check_call(h, projected, pitch, requests, slots, core_out);
+    if (st != KDA_OK || requests == 0) return st;
+    if (accepted == nullptr) return KDA_ERR_NULL;
+    if (!aligned(accepted, 4)) return KDA_ERR_ALIGN;
+    if ((int64_t)requests * tokens > INT32_MAX) return KDA_ERR_SHAPE;
+    const kda::CoreParams p =
+        core_params(h, projected, pitch, requests, slots, slots_row_stride, accepted, core_out);
+    hipError_t e = kda::launch_core(tokens, p, static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? KDA_OK : hip_fail(e, "kda_verify launch");
+}
+
+kda_status kda_device_errors(kda_handle h, int32_t* count_out, void* hip_stream) {
+    if (h == nullptr || count_out == nullptr) return KDA_ERR_NULL;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    int32_t host = 0;
+    hipError_t e = hipMemcpyAsync(&host, h->err_count, sizeof host, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemsetAsync(h->err_count, 0, sizeof(int32_t), s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "kda_device_errors");
+    *count_out = host;
+    return KDA_OK;
+}
+
+kda_status kda_destroy(kda_handle h) {
+    if (h == nullptr) return KDA_OK;
+    hipError_t e = hipDeviceSynchronize();
+    hipError_t f = hipFree(h->dev_mem);
+    delete h;
+    if (e != hipSuccess) return hip_fail(e, "kda_destroy sync");
+    if (f != hipSuccess) return hip_fail(f, "kda_destroy free");
+    return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,384 @@
+// gfx950 kernels of the KDA decode / spec-verify core.
+//
+// Sources (page titles, sections):
+//   [kda]      "vllm.models.kimi_k3.amd.specialized_decode.mono.attention.kda",
+//              module docstring, "kda tasks" row: inputs that need no hand-off
+//              are loaded first (conv window, state rows, f_b rows), then the
+//              conv update, f_b MFMA + lower-bound gate, l2norm, the
+//              recurrence on 16 state rows with a state written per token, and
+//              the gated RMSNorm over the head's 128 outputs -> core_out.
+//   [prepared] "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.kda.prepared",
+//              PreparedKda._operands (packed projection row), decode_conv_weight.
+//
+// One workgroup owns one (request, head) unit for all L tokens: 512 threads,
+// wave w holds state rows v = 16w .. 16w + 15 in registers across the token
+// loop (the pages split a head into eight 16-row v-chunks on separate CTAs
+// that trade q/k and norm partials through mailboxes; here the eight chunks
+// are the eight waves of one workgroup and the hand-offs go through LDS).
+//
+// Lane layout of the state: lane l of wave w holds rows 16w + (l >> 3) and
+// 16w + 8 + (l >> 3), columns 32m + 4(l & 7) .. +3 for m = 0..3. One dwordx4
+// load or store instruction therefore covers eight full 128-byte lines
+// (eight rows x 128 B), and a row's dot product is an 8-lane reduction done
+// with three DPP steps.
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) {
+    return __uint_as_float(bits << 16);
+}
+
+// Round to nearest even (gfx950 converts fp32 -> bf16 in hardware).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ float exp_fast(float x) {
+    return __builtin_amdgcn_exp2f(x * kLog2e);
+}
+
+// 1 / (1 + e^-x): saturates to 0 at -inf and 1 at +inf without overflow.
+__device__ __forceinline__ float sigmoid(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + exp_fast(-x));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 8 lanes l with the same l >> 3 (one state row).
+__device__ __forceinline__ float sum8(float x) {
+    x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]: partner lane ^ 1
+    x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]: partner lane ^ 2
+    x += dpp<0x141>(x);  // row_half_mirror: partner lane 7 - i of the 8
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b, float acc) {
+    acc = __builtin_fmaf(a.x, b.x, acc);
+    acc = __builtin_fmaf(a.y, b.y, acc);
+    acc = __builtin_fmaf(a.z, b.z, acc);
+    acc = __builtin_fmaf(a.w, b.w, acc);
+    return acc;
+}
+
+template <int L>
+__global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) {
+    constexpr int N = kHeadDim;
+    const int H = p.heads;
+    const int D = H * N;
+    const int r = blockIdx.x / H;
+    const int h = blockIdx.x - r * H;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+
+    __shared__ float s_qkv[L][3 * N];   // conv outputs; q, k normalised in place
+    __shared__ float s_eg[L][N];        // e^g per key channel
+    __shared__ float s_gate[L][N];      // output gate (raw)
+    __shared__ float s_o[L][N];         // recurrence outputs
+    __shared__ float s_braw[L];
+    __shared__ float s_beta[L];
+    __shared__ float s_kq[L];           // k_hat . q_hat
+
+    // ---- slot resolution ([prepared] run: slots [B], or [>= B, q] + accepted)
+    const int32_t* srow = p.slots + (int64_t)r * p.slots_row_stride;
+    int dst[L];
+    bool ok = true;
+#pragma unroll
+    for (int t = 0; t < L; ++t) {
+        dst[t] = srow[t];
+        ok = ok && (unsigned)dst[t] < (unsigned)p.num_slots;
+    }
+    int src = dst[0];
+    if (p.accepted != nullptr) {
+        const int a = p.accepted[r];
+        ok = ok && a >= 1 && a <= L;
+        src = ok ? srow[a - 1] : 0;
+    }
+    if (!ok) {  // uniform across the workgroup: skip the whole request
+        if (h == 0 && tid == 0) atomicAdd(p.err_count, 1);
+        return;
+    }
+
+    const int64_t row0 = (int64_t)r * L;
+    const uint16_t* prow = p.projected + row0 * p.pitch;
+
+    // ---- small inputs first: conv window + x (waves 0-5), gate + beta (6-7)
+    const bool conv_thread = tid < 3 * N;
+    const int cl = conv_thread ? tid : tid - 3 * N;   // conv channel, or gate column
+    const int cs = cl >> 7;                           // 0 q, 1 k, 2 v
+    const int cj = cl & (N - 1);
+    const int64_t cch = (int64_t)cs * D + (int64_t)h * N + cj;   // channel in 0 .. 3D
+    uint32_t win[kWidth - 1];
+    uint32_t xb[L];
+    float cw[kWidth];
+    float cb = 0.0f;
+    uint32_t braw = 0;
+    if (conv_thread) {
+        const int64_t cbase = (int64_t)src * p.conv_slot_stride + cch * p.conv_dim_stride;
+#pragma unroll
+        for (int m = 0; m < kWidth - 1; ++m) win[m] = p.conv[cbase + m * p.conv_pos_stride];
+#pragma unroll
+        for (int t = 0; t < L; ++t) xb[t] = prow[t * p.pitch + cch];
+#pragma unroll
+        for (int j = 0; j < kWidth; ++j)
+            cw[j] = p.conv_w[(int64_t)(cs * kWidth + j) * D + (int64_t)h * N + cj];
+        cb = p.conv_b[cch];
+    } else {
+#pragma unroll
+        for (int t = 0; t < L; ++t) xb[t] = prow[t * p.pitch + 3 * (int64_t)D + (int64_t)h * N + cj];
+        if (cj < L) braw = prow[cj * p.pitch + 4 * (int64_t)D + kFaRank + h];
+    }
+
+    // ---- gate MFMA operands: wave w computes outputs 16w .. 16w + 15 of the head
+    const int mn = lane & 15;        // A row (token) / B column (output)
+    const int kg = lane >> 4;        // which 8 of each 32-wide K step
+    const int i_out = wave * 16 + mn;
+    bf16x8 bfrag[4];
+    {
+        const uint16_t* fb = p.f_b + (int64_t)(h * N + i_out) * kFaRank + 8 * kg;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            bfrag[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(fb + 32 * s));
+    }
+    bf16x8 afrag[4];
+    if (mn < L) {   // rows are only 4-byte aligned: dword loads
+        const uint32_t* fa = reinterpret_cast<const uint32_t*>(prow + mn * p.pitch + 4 * (int64_t)D + 8 * kg);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            u32x4 v = {fa[16 * s + 0], fa[16 * s + 1], fa[16 * s + 2], fa[16 * s + 3]};
+            afrag[s] = __builtin_bit_cast(bf16x8, v);
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) afrag[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    }
+    const float dtv = p.dt_bias[h * N + i_out];
+    const float aexp = p.a_exp[h];
+    float nw0 = 0.0f, nw1 = 0.0f;
+    if (wave < L) {
+        nw0 = p.norm_w[h * N + 2 * lane];
+        nw1 = p.norm_w[h * N + 2 * lane + 1];
+    }
+
+    // ---- the carried state: 64 KiB a unit, streamed once
+    const int rsub = lane >> 3;
+    const int csub = (lane & 7) * 4;
+    const int64_t unit_off = (int64_t)h * N * N + (int64_t)(wave * 16 + rsub) * N + csub;
+    f32x4 S[2][4];
+    {
+        const float* sb = p.state + (int64_t)src * p.state_slot_stride + unit_off;
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                S[g][m] = __builtin_nontemporal_load(
+                    reinterpret_cast<const f32x4*>(sb + g * 8 * N + 32 * m));
+    }
+
+    // ---- conv update + SiLU; the window after token t goes to slot dst[t]
+    if (conv_thread) {
+        float w0 = bf16_to_f32(win[0]), w1 = bf16_to_f32(win[1]), w2 = bf16_to_f32(win[2]);
+        uint32_t b0 = win[0], b1 = win[1], b2 = win[2];
+#pragma unroll
+        for (int t = 0; t < L; ++t) {
+            const float x = bf16_to_f32(xb[t]);
+            float pre = __builtin_fmaf(cw[0], w0, cb);
+            pre = __builtin_fmaf(cw[1], w1, pre);
+            pre = __builtin_fmaf(cw[2], w2, pre);
+            pre = __builtin_fmaf(cw[3], x, pre);
+            s_qkv[t][cl] = pre * sigmoid(pre);
+            w0 = w1; w1 = w2; w2 = x;
+            b0 = b1; b1 = b2; b2 = xb[t];
+            uint16_t* cw_out = p.conv + (int64_t)dst[t] * p.conv_slot_stride + cch * p.conv_dim_stride;
+            cw_out[0] = (uint16_t)b0;
+            cw_out[p.conv_pos_stride] = (uint16_t)b1;
+            cw_out[2 * p.conv_pos_stride] = (uint16_t)b2;
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < L; ++t) s_gate[t][cj] = bf16_to_f32(xb[t]);
+        if (cj < L) s_braw[cj] = bf16_to_f32(braw);
+    }
+
+    // ---- g1 = f_b f_a on MFMA (tokens padded to 16), then the lower-bound gate
+    {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[s], bfrag[s], acc, 0, 0, 0);
+        // lane holds tokens 4 kg + i, output column mn
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * kg + i;
+            if (t < L) {
+                const float g = p.lb * sigmoid(aexp * (acc[i] + dtv));
+                s_eg[t][i_out] = exp_fast(g);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- l2norm of q and k, beta, k_hat . q_hat: wave t for token t
+    if (wave < L) {
+        const int t = wave;
+        float q0 = s_qkv[t][2 * lane], q1 = s_qkv[t][2 * lane + 1];
+        float k0 = s_qkv[t][N + 2 * lane], k1 = s_qkv[t][N + 2 * lane + 1];
+        const float sq = wave_sum(q0 * q0 + q1 * q1);
+        const float sk = wave_sum(k0 * k0 + k1 * k1);
+        const float qs = p.q_scale * __builtin_amdgcn_rsqf(sq + p.l2_eps);
+        const float ks = __builtin_amdgcn_rsqf(sk + p.l2_eps);
+        q0 *= qs; q1 *= qs; k0 *= ks; k1 *= ks;
+        s_qkv[t][2 * lane] = q0;
+        s_qkv[t][2 * lane + 1] = q1;
+        s_qkv[t][N + 2 * lane] = k0;
+        s_qkv[t][N + 2 * lane + 1] = k1;
+        const float kq = wave_sum(q0 * k0 + q1 * k1);
+        if (lane == 0) {
+            s_beta[t] = sigmoid(s_braw[t]);
+            s_kq[t] = kq;
+        }
+    }
+    __syncthreads();
+
+    // ---- the recurrence over the L tokens, a state stored per token
+#pragma unroll
+    for (int t = 0; t < L; ++t) {
+        f32x4 eg[4], kk[4], qq[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            eg[m] = *reinterpret_cast<const f32x4*>(&s_eg[t][32 * m + csub]);
+            qq[m] = *reinterpret_cast<const f32x4*>(&s_qkv[t][32 * m + csub]);
+            kk[m] = *reinterpret_cast<const f32x4*>(&s_qkv[t][N + 32 * m + csub]);
+        }
+        const float beta = s_beta[t];
+        const float kq = s_kq[t];
+        float* dp = p.state + (int64_t)dst[t] * p.state_slot_stride + unit_off;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const int row = wave * 16 + g * 8 + rsub;
+            float a = 0.0f, b = 0.0f;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                S[g][m] *= eg[m];                 // decay: column i scaled by e^g_i
+                a = dot4(S[g][m], kk[m], a);      // (S k)_row, decayed state
+                b = dot4(S[g][m], qq[m], b);      // (S q)_row, decayed state
+            }
+            a = sum8(a);
+            b = sum8(b);
+            const float bu = beta * (s_qkv[t][2 * N + row] - a);
+            // o = (S_decayed + bu k^T) q = b + bu (k . q)
+            const float o = __builtin_fmaf(bu, kq, b);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                S[g][m] += bu * kk[m];
+                __builtin_nontemporal_store(S[g][m],
+                                            reinterpret_cast<f32x4*>(dp + g * 8 * N + 32 * m));
+            }
+            if ((lane & 7) == 0) s_o[t][row] = o;
+        }
+    }
+    __syncthreads();
+
+    // ---- gated RMSNorm over the head's 128 outputs -> bf16 core_out: wave t for token t
+    if (wave < L) {
+        const int t = wave;
+        const float o0 = s_o[t][2 * lane], o1 = s_o[t][2 * lane + 1];
+        const float ss = wave_sum(o0 * o0 + o1 * o1);
+        const float rstd = __builtin_amdgcn_rsqf(ss * (1.0f / N) + p.norm_eps);
+        const float y0 = o0 * rstd * nw0 * sigmoid(s_gate[t][2 * lane]);
+        const float y1 = o1 * rstd * nw1 * sigmoid(s_gate[t][2 * lane + 1]);
+        const uint32_t packed = f32_to_bf16(y0) | (f32_to_bf16(y1) << 16);
+        uint32_t* op = reinterpret_cast<uint32_t*>(p.out + (row0 + t) * D + (int64_t)h * N + 2 * lane);
+        *op = packed;
+    }
+}
+
+// Weight re-layout at prepare time ([prepared] PreparedKda.__init__ and
+// decode_conv_weight): conv weight [3D][1][W] -> fp32 [3][W][D], bias -> fp32
+// (zeros if absent), f_b copied, A_log -> exp(A_log), dt_bias copied, norm
+// weight expanded to [H][128]. One grid-stride pass over all items.
+__global__ void kda_prepare_kernel(const PrepareParams in, const PreparedWeights out) {
+    const int64_t H = in.heads, D = H * kHeadDim, C = 3 * D;
+    const int64_t n_w = C * kWidth, n_b = C, n_fb = D * kFaRank, n_a = H, n_dt = D,
+                  n_nw = H * kHeadDim;
+    const int64_t total = n_w + n_b + n_fb + n_a + n_dt + n_nw;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        int64_t i = e;
+        if (i < n_w) {   // i = (s * W + j) * D + d  <-  weight[(s * D + d) * W + j]
+            const int64_t d = i % D, sj = i / D, j = sj % kWidth, s = sj / kWidth;
+            out.conv_w[i] = bf16_to_f32(in.conv_weight[(s * D + d) * kWidth + j]);
+            continue;
+        }
+        i -= n_w;
+        if (i < n_b) {
+            out.conv_b[i] = in.conv_bias ? bf16_to_f32(in.conv_bias[i]) : 0.0f;
+            continue;
+        }
+        i -= n_b;
+        if (i < n_fb) {
+            out.f_b[i] = in.f_b[i];
+            continue;
+        }
+        i -= n_fb;
+        if (i < n_a) {
+            out.a_exp[i] = expf(in.A_log[i]);
+            continue;
+        }
+        i -= n_a;
+        if (i < n_dt) {
+            out.dt_bias[i] = in.dt_bias[i];
+            continue;
+        }
+        i -= n_dt;
+        out.norm_w[i] = in.norm_weight[(i / kHeadDim) * in.norm_head_stride + i % kHeadDim];
+    }
+}
+
+template <int L>
+hipError_t launch_core_t(const CoreParams& p, hipStream_t s) {
+    const dim3 grid((unsigned)(p.requests * p.heads)), block(kThreads);
+    hipLaunchKernelGGL(kda_core_kernel<L>, grid, block, 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prepare(const PrepareParams& in, const PreparedWeights& out, hipStream_t s) {
+    hipLaunchKernelGGL(kda_prepare_kernel, dim3(256), dim3(256), 0, s, in, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_core(int tokens, const CoreParams& p, hipStream_t s) {
+    switch (tokens) {
+        case 1: return launch_core_t<1>(p, s);
+        case 2: return launch_core_t<2>(p, s);
+        case 3: return launch_core_t<3>(p, s);
+        case 4: return launch_core_t<4>(p, s);
+        case 5: return launch_core_t<5>(p, s);
+        case 6: return launch_core_t<6>(p, s);
+        case 7: return launch_core_t<7>(p, s);
+        case 8: return launch_core_t<8>(p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace kda

@@ -1,0 +1,69 @@
+// Internal interface between the host library (kda_api.cpp) and the gfx950
+// kernels (kda_core.hip). Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kHeadDim = 128;   // dk = dv
+constexpr int kFaRank = 128;    // f_a width
+constexpr int kWidth = 4;       // conv taps
+constexpr int kMaxTokens = 8;   // verify length bound
+constexpr int kThreads = 512;   // 8 waves of 64: wave w owns state rows 16w .. 16w + 15
+
+// Weights in the layout the core kernel reads, owned by a handle.
+struct PreparedWeights {
+    float* conv_w;        // fp32 [3][W][D]: tap j of channel (s, d) at (s * W + j) * D + d
+    float* conv_b;        // fp32 [3D] (zeros when the layer has no conv bias)
+    uint16_t* f_b;        // bf16 [D][128]
+    float* a_exp;         // fp32 [H] = exp(A_log)
+    float* dt_bias;       // fp32 [D]
+    float* norm_w;        // fp32 [H][128]
+};
+
+// Everything one launch of the core kernel reads, by value.
+struct CoreParams {
+    const uint16_t* projected;  // bf16 rows, pitch elements apart
+    int64_t pitch;
+    const int32_t* slots;
+    int64_t slots_row_stride;
+    const int32_t* accepted;    // nullptr: decode (src = dst = slots[r])
+    uint16_t* conv;
+    int64_t conv_slot_stride, conv_dim_stride, conv_pos_stride;
+    float* state;
+    int64_t state_slot_stride;
+    const float* conv_w;
+    const float* conv_b;
+    const uint16_t* f_b;
+    const float* a_exp;
+    const float* dt_bias;
+    const float* norm_w;
+    uint16_t* out;
+    int32_t* err_count;
+    int32_t heads;
+    int32_t requests;
+    int32_t num_slots;
+    float lb;
+    float q_scale;
+    float norm_eps;
+    float l2_eps;
+};
+
+// Raw inputs of the weight re-layout kernel (device pointers).
+struct PrepareParams {
+    const uint16_t* conv_weight;  // bf16 [3D][1][W]
+    const uint16_t* conv_bias;    // bf16 [3D] or nullptr
+    const uint16_t* f_b;          // bf16 [D][128]
+    const float* A_log;           // [H]
+    const float* dt_bias;         // [D]
+    const float* norm_weight;     // [128] or [H][128]
+    int32_t norm_head_stride;
+    int32_t heads;
+};
+
+hipError_t launch_prepare(const PrepareParams& in, const PreparedWeights& out, hipStream_t s);
+hipError_t launch_core(int tokens, const CoreParams& p, hipStream_t s);
+
+}  // namespace kda

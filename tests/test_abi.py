@@ -1,0 +1,124 @@
+"""The C-ABI library loads, exports every function include/kda.h declares, and its
+host-side validation answers without a GPU (no call here reaches the device)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
+
+import kimi_delta_attention_conv_amd as kda  # noqa: E402
+
+
+def declared_functions():
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names.update(re.findall(r"^\s*(?:const\s+)?[\w\*\s]+?\b(kda_\w+)\s*\(", text,
+                                flags=re.M))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built (run __graft_entry__.build())")
+    return kda.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("kda_prepare", "kda_decode", "kda_verify", "kda_device_errors", "kda_destroy",
+              "kda_status_string", "kda_last_hip_error", "kda_probe_copy", "kda_probe_write",
+              "kda_probe_read", "kda_probe_sink_floats"):
+        assert n in names, n
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for n in declared_functions():
+        assert n in exported, f"{n} declared in kda.h but not exported"
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    seen = set()
+    for code in range(0, -7, -1):
+        s = kda.kda_status_string(code)
+        assert s and s not in seen
+        seen.add(s)
+    assert lib.kda_last_hip_error() == b""
+
+
+def _weights(**kw):
+    fake = 0x10000  # never dereferenced: validation fails before any HIP call
+    base = dict(heads=2, conv_width=4, conv_weight=fake, conv_bias=None, f_b=fake, A_log=fake,
+                dt_bias=fake, norm_weight=fake, norm_head_stride=0, gate_lower_bound=-5.0,
+                norm_eps=1e-6, l2_eps=1e-6)
+    base.update(kw)
+    return kda.KdaWeights(**base)
+
+
+def _caches(**kw):
+    D = 256
+    base = dict(conv=0x20000, conv_slot_stride=9 * D, conv_dim_stride=3, conv_pos_stride=1,
+                state=0x40000, state_slot_stride=2 * 128 * 128, num_slots=4)
+    base.update(kw)
+    return kda.KdaCaches(**base)
+
+
+@pytest.mark.parametrize("weights,caches,status", [
+    (None, _caches(), -1),
+    (_weights(f_b=None), _caches(), -1),
+    (_weights(), _caches(state=None), -1),
+    (_weights(heads=0), _caches(), -2),
+    (_weights(conv_width=3), _caches(), -4),
+    (_weights(norm_head_stride=64), _caches(), -2),
+    (_weights(norm_eps=float("nan")), _caches(), -2),
+    (_weights(l2_eps=-1.0), _caches(), -2),
+    (_weights(), _caches(num_slots=0), -2),
+    (_weights(), _caches(state_slot_stride=128 * 128), -2),
+    (_weights(), _caches(conv_slot_stride=100), -2),
+    (_weights(), _caches(conv_dim_stride=-3), -2),
+    (_weights(), _caches(state=0x40004), -3),
+    (_weights(), _caches(state_slot_stride=2 * 128 * 128 + 2), -3),
+    (_weights(A_log=0x10002), _caches(), -3),
+], ids=lambda v: str(v) if isinstance(v, int) else "")
+def test_prepare_validation_without_gpu(lib, weights, caches, status):
+    h = ctypes.c_void_p()
+    wp = None if weights is None else ctypes.byref(weights)
+    got = lib.kda_prepare(wp, ctypes.byref(caches), None, ctypes.byref(h))
+    assert got == status
+    assert h.value is None
+
+
+def test_probe_validation_without_gpu(lib):
+    assert lib.kda_probe_copy(None, 0x1000, 16, None) == -1
+    assert lib.kda_probe_write(0x1008, 16, 1.0, None) == -3
+    assert lib.kda_probe_read(0x1000, 24, 0x2000, None) == -3
+    assert lib.kda_probe_sink_floats() > 0
+
+
+def test_calls_on_null_handle(lib):
+    n = ctypes.c_int32(7)
+    assert lib.kda_decode(None, 0x1000, 1154, 1, 0x2000, 0x3000, None) == -1
+    assert lib.kda_verify(None, 0x1000, 1154, 1, 4, 0x2000, 4, 0x4000, 0x3000, None) == -1
+    assert lib.kda_device_errors(None, ctypes.byref(n), None) == -1
+    assert n.value == 7
+    assert lib.kda_destroy(None) == 0
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    saved = kda._lib
+    try:
+        kda._lib = None
+        with pytest.raises(ImportError):
+            kda.load_library(str(tmp_path / "missing.so"))
+    finally:
+        kda._lib = saved

@@ -1,0 +1,196 @@
+"""Structural, bit-exact properties of the HIP path (through the C ABI).
+
+Identity mode (g = 0, beta = 0) shows slot and accepted-count selection bit for
+bit; decode equals a one-token verify; verify over L tokens equals L chained
+decodes; both conv layouts, strided slots, a padded pitch, per-head norm
+weights and no conv bias are handled; invalid requests are skipped and counted;
+an empty call is a no-op; host validation rejects bad arguments and leaves the
+device untouched."""
+import numpy as np
+import pytest
+import torch
+
+from kda_inputs import make_case, make_config
+from oracle_cases import run_oracle
+from parity import assert_parity, request_slots
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _identity_projected(case):
+    proj = case.projected.clone()
+    D = case.D
+    proj[:, 4 * D + 128: 4 * D + 128 + case.H] = float("-inf")   # beta = 0
+    return proj
+
+
+@pytest.mark.parametrize("which", ["small", "verify_r64_l8"])
+def test_identity_mode_selects_accepted_state_bit_exact(which):
+    from gpu_cases import run_gpu
+    case = make_case(R=9, L=5, H=2, num_slots=64, seed=400, verify=True) if which == "small" \
+        else make_config(3)
+    print(f"[case] identity mode {which}", flush=True)
+    proj = _identity_projected(case)
+    got = run_gpu(case, projected=proj, gate_lower_bound=0.0)
+    before = case.state.numpy()
+    assert got["errors"] == 0
+    for r, (ok, src, dst) in enumerate(request_slots(case)):
+        assert ok
+        for t, d in enumerate(dst):
+            assert np.array_equal(got["state"][d], before[src]), (r, t)
+
+
+def test_decode_equals_single_token_verify_bit_exact():
+    from gpu_cases import run_gpu
+    case = make_case(R=20, L=1, H=3, num_slots=40, seed=401, verify=False)
+    a = run_gpu(case)
+    b = run_gpu(case, accepted=torch.ones(case.R, dtype=torch.int32), decode=False)
+    for k in ("out", "conv", "state"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_verify_equals_chained_decodes_bit_exact():
+    """The kernel's per-token arithmetic does not depend on L: a verify call and L
+    decode calls chained on one slot agree bit for bit."""
+    from gpu_cases import GpuCase
+    case = make_case(R=4, L=6, H=2, num_slots=32, seed=402, verify=True)
+    g = GpuCase(case).run()
+    full = g.host()
+    g.close()
+    reqs = request_slots(case)
+    for r, (ok, src, dst) in enumerate(reqs):
+        dec = make_case(R=1, L=1, H=2, num_slots=32, seed=402, verify=False)
+        dec.conv_weight, dec.conv_bias, dec.f_b = case.conv_weight, case.conv_bias, case.f_b
+        dec.A_log, dec.dt_bias, dec.norm_weight = case.A_log, case.dt_bias, case.norm_weight
+        state = case.state.clone()
+        conv = case.conv_storage.clone()
+        tmp = dst[0]
+        state[tmp] = state[src]
+        conv[tmp] = conv[src]
+        dec.state, dec.conv_storage = state, conv
+        dec.slots = torch.tensor([tmp], dtype=torch.int32)
+        gd = GpuCase(dec)
+        try:
+            for t in range(case.L):
+                row = r * case.L + t
+                gd.run(projected=case.projected[row:row + 1])
+                h = gd.host()
+                assert np.array_equal(h["out"][0], full["out"][row]), (r, t)
+                assert np.array_equal(h["state"][tmp], full["state"][dst[t]]), (r, t)
+                assert np.array_equal(h["conv"][tmp], full["conv"][dst[t]]), (r, t)
+        finally:
+            gd.close()
+
+
+def test_conv_layouts_agree_bit_exact():
+    from gpu_cases import run_gpu
+    a = make_case(R=6, L=3, H=2, num_slots=32, seed=403, verify=True, conv_dim_first=True)
+    b = make_case(R=6, L=3, H=2, num_slots=32, seed=403, verify=True, conv_dim_first=True)
+    b.conv_dim_first = False
+    b.conv_storage = a.conv_storage.transpose(1, 2).contiguous()
+    ra, rb = run_gpu(a), run_gpu(b)
+    assert np.array_equal(ra["out"], rb["out"])
+    assert np.array_equal(ra["state"], rb["state"])
+    assert np.array_equal(ra["conv"], rb["conv"].transpose(0, 2, 1))
+
+
+def test_strided_block_table_slots_equal_contiguous_copy():
+    from gpu_cases import run_gpu
+    case = make_case(R=8, L=4, H=2, num_slots=96, seed=404, verify=True, block_table_cols=11)
+    assert case.slots.stride(0) == 11
+    a = run_gpu(case)
+    b = run_gpu(case, slots=case.slots.contiguous())
+    for k in ("out", "conv", "state"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_invalid_requests_are_skipped_and_counted():
+    from gpu_cases import run_gpu
+    case = make_case(R=6, L=3, H=2, num_slots=24, seed=405, verify=True)
+    s = case.slots.clone()
+    acc = case.accepted.clone()
+    s[1, 0] = case.num_slots       # out of range
+    s[3, 2] = -1                   # negative
+    acc[4] = 0                     # not in 1..L
+    acc[5] = case.L + 1
+    case.slots, case.accepted = s, acc
+    before = case.state.numpy().copy()
+    ref = run_oracle(case)
+    got = run_gpu(case)
+    assert ref["skipped"] == 4
+    assert_parity(case, ref, got, before, label="invalid requests")
+
+
+def test_empty_call_is_a_noop():
+    from gpu_cases import GpuCase
+    case = make_case(R=2, L=2, H=2, num_slots=8, seed=406, verify=True)
+    g = GpuCase(case)
+    try:
+        before = g.state.clone()
+        empty = torch.empty(0, case.pitch, dtype=torch.bfloat16, device="cuda")
+        out = torch.empty(0, case.D, dtype=torch.bfloat16, device="cuda")
+        slots = torch.empty(0, 2, dtype=torch.int32, device="cuda")
+        g.core.verify(empty, out, slots, torch.empty(0, dtype=torch.int32, device="cuda"))
+        g.core.decode(empty, out, torch.empty(0, dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+        assert torch.equal(before, g.state)
+        assert g.core.device_errors() == 0
+    finally:
+        g.close()
+
+
+def test_padded_pitch_per_head_norm_and_no_bias():
+    from gpu_cases import run_gpu
+    case = make_case(R=5, L=2, H=3, num_slots=24, seed=407, verify=True, with_bias=False,
+                     pitch=4 * 384 + 128 + 3 + 11)
+    nw = torch.rand(case.H, 128, generator=torch.Generator().manual_seed(9)) + 0.5
+    before = case.state.numpy().copy()
+    ref = run_oracle(case, norm_weight=nw.numpy().reshape(-1), norm_head_stride=128)
+    got = run_gpu(case, norm_weight=nw)
+    assert_parity(case, ref, got, before, label="padded pitch, per-head norm, no bias")
+
+
+def test_host_validation_leaves_device_untouched():
+    import kimi_delta_attention_conv_amd as kda
+    from gpu_cases import GpuCase
+    case = make_case(R=2, L=3, H=2, num_slots=8, seed=408, verify=True)
+    g = GpuCase(case)
+    try:
+        before = g.state.clone()
+        h = g.core.handle
+        p, o = g.projected, g.out
+        slots = case.slots.cuda()
+        acc = case.accepted.cuda()
+        cases = [
+            (lambda: kda.kda_verify(h, p.data_ptr(), case.pitch - 2, 2, 3, slots.data_ptr(), 3,
+                                    acc.data_ptr(), o.data_ptr()), -2),
+            (lambda: kda.kda_verify(h, p.data_ptr(), case.pitch + 1, 2, 3, slots.data_ptr(), 3,
+                                    acc.data_ptr(), o.data_ptr()), -2),
+            (lambda: kda.kda_verify(h, p.data_ptr(), case.pitch, 2, 9, slots.data_ptr(), 9,
+                                    acc.data_ptr(), o.data_ptr()), -4),
+            (lambda: kda.kda_verify(h, p.data_ptr(), case.pitch, 2, 3, slots.data_ptr(), 2,
+                                    acc.data_ptr(), o.data_ptr()), -2),
+            (lambda: kda.kda_verify(h, p.data_ptr(), case.pitch, 2, 3, slots.data_ptr(), 3,
+                                    0, o.data_ptr()), -1),
+            (lambda: kda.kda_verify(h, p.data_ptr() + 2, case.pitch, 2, 3, slots.data_ptr(), 3,
+                                    acc.data_ptr(), o.data_ptr()), -3),
+            (lambda: kda.kda_decode(h, p.data_ptr(), case.pitch, -1, slots.data_ptr(),
+                                    o.data_ptr()), -2),
+            (lambda: kda.kda_decode(h, p.data_ptr(), case.pitch, 2, slots.data_ptr(),
+                                    o.data_ptr() + 2), -3),
+        ]
+        for fn, status in cases:
+            with pytest.raises(kda.KdaError) as ei:
+                fn()
+            assert ei.value.status == status
+        torch.cuda.synchronize()
+        assert torch.equal(before, g.state)
+        assert g.core.device_errors() == 0
+    finally:
+        g.close()
