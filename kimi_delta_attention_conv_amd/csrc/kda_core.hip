@@ -178,7 +178,11 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
         nw1 = p.norm_w[h * N + 2 * lane + 1];
     }
 
-    // ---- the carried state: 64 KiB a unit, streamed once
+    // ---- the carried state: 64 KiB a unit, read once. A one-token call
+    // overwrites the tile it reads (in place), and a plain load would leave its
+    // lines in L2 just before the non-temporal stores replace them; there the
+    // load is non-temporal too. With L > 1 the tokens write other slots and
+    // plain loads measured faster on MI355X.
     const int rsub = lane >> 3;
     const int csub = (lane & 7) * 4;
     const int64_t unit_off = (int64_t)h * N * N + (int64_t)(wave * 16 + rsub) * N + csub;
@@ -188,9 +192,10 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-                S[g][m] = __builtin_nontemporal_load(
-                    reinterpret_cast<const f32x4*>(sb + g * 8 * N + 32 * m));
+            for (int m = 0; m < 4; ++m) {
+                const f32x4* ptr = reinterpret_cast<const f32x4*>(sb + g * 8 * N + 32 * m);
+                S[g][m] = (L == 1) ? __builtin_nontemporal_load(ptr) : *ptr;
+            }
     }
 
     // ---- conv update + SiLU; the window after token t goes to slot dst[t]
