@@ -83,8 +83,16 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
     constexpr int N = kHeadDim;
     const int H = p.heads;
     const int D = H * N;
-    const int r = blockIdx.x / H;
-    const int h = blockIdx.x - r * H;
+    // XCD-blocked unit order: the dispatcher sends workgroup b to XCD b % 8, so
+    // XCD x takes a contiguous block of (request, head) units (measured 1.5-2 %
+    // faster than request-major order on MI355X; any order is correct).
+    int unit = blockIdx.x;
+    {
+        const int q = (p.requests * H) >> 3;
+        if ((int)blockIdx.x < 8 * q) unit = (blockIdx.x & 7) * q + (blockIdx.x >> 3);
+    }
+    const int r = unit / H;
+    const int h = unit - r * H;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
