@@ -52,6 +52,9 @@ def parse_args():
     ap.add_argument("--probe", action="store_true", help="also run the HBM probes")
     ap.add_argument("--probe-only", action="store_true",
                     help="run only the HBM probes (counter calibration)")
+    ap.add_argument("--proj", action="store_true",
+                    help="time the in_proj / o_proj projections at the workload's row count "
+                         "instead of the core (prints one JSON line)")
     return ap.parse_args()
 
 
@@ -118,6 +121,57 @@ def probe(torch, kda):
     return res
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def bench_projections(args, torch, kda):
+    """in_proj [S, 7168] x [4D+128+H, 7168]^T and o_proj [S, D] x [7168, D]^T on MFMA."""
+    from kda_inputs import CONFIGS, HIDDEN, make_linear
+    cfg = CONFIGS[args.config]
+    S, H = cfg["R"] * cfg["L"], cfg["H"]
+    D = 128 * H
+    lib = kda.load_library()
+    sp = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for name, (N, K) in (("in_proj", (4 * D + 128 + H, HIDDEN)), ("o_proj", (HIDDEN, D))):
+        x, w = make_linear(S, N, K, seed=7)
+        # several weight copies rotate so that the timed launches stream from HBM
+        copies = max(1, -(-(600 << 20) // (N * K * 2)))
+        xs = x.cuda()
+        ws = [w.cuda() for _ in range(copies)]
+        y = torch.empty(S, N, dtype=torch.bfloat16, device="cuda")
+
+        def launch(i):
+            return lib.kda_linear(xs.data_ptr(), xs.stride(0), ws[i % copies].data_ptr(),
+                                  y.data_ptr(), N, S, N, K, sp)
+        for i in range(args.warmup):
+            assert launch(i) == 0
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            launch(i)
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        flops = 2.0 * S * N * K
+        nbytes = (N * K + S * K + S * N) * 2
+        tflops = flops / (ms * 1e-3) / 1e12
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        t_mfma, t_hbm = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12), nbytes / (HBM_PEAK_GBPS * 1e9)
+        bound = "mfma" if t_mfma >= t_hbm else "hbm"
+        out[name] = {"M": S, "N": N, "K": K, "us": round(ms * 1e3, 2),
+                     "tflops": round(tflops, 1), "gbps": round(gbps, 1),
+                     "roofline": {"bound": bound,
+                                  "achieved": round(tflops if bound == "mfma" else gbps, 1),
+                                  "peak": MFMA_BF16_PEAK_TFLOPS if bound == "mfma" else HBM_PEAK_GBPS,
+                                  "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+                                  "frac": round((t_mfma if bound == "mfma" else t_hbm) / (ms * 1e-3), 4)}}
+        del ws, xs, y
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(case, seconds):
     """The oracle, as it stands, timed on the host on the same workload."""
     import numpy as np
@@ -179,6 +233,10 @@ def main():
 
     if args.probe_only:
         print(json.dumps({"hbm_probe": probe(torch, kda)}), flush=True)
+        return
+    if args.proj:
+        print(json.dumps({"projections": bench_projections(args, torch, kda),
+                          "workload_rows_of": make_config(args.config).name}), flush=True)
         return
 
     case = make_config(args.config)

@@ -161,6 +161,40 @@ kda_status kda_verify(kda_handle h, const void* projected, int64_t pitch, int32_
                       int32_t tokens, const int32_t* slots, int64_t slots_row_stride,
                       const int32_t* accepted, void* core_out, void* hip_stream);
 
+/* ---- projections around the core ------------------------------------------
+ * The dense contraction y = x W^T of an nn.Linear layer without bias: bf16
+ * inputs, fp32 accumulation (MFMA), bf16 output rounded to nearest even.
+ * One rank's share of the layer's projections on each side of the core:
+ *   in_proj  ([kda] module docstring, gemv role: in_proj -> q|k|v|g|f_a|beta):
+ *            hidden rows [S][hidden] x W_in [4D + 128 + H][hidden] -> the
+ *            packed projection rows [S][pitch] that kda_decode / kda_verify read;
+ *   o_proj   (page "vllm.models.kimi_k3.amd.specialized_decode.mono.attention.back",
+ *            module docstring: o_proj with K = 1536 local): core_out rows
+ *            [S][D] x W_o [hidden][D] -> this rank's partial [S][hidden],
+ *            before the tensor-parallel all-reduce (not part of this library).
+ * Layouts: x rows x_pitch elements apart, base and rows 16-byte aligned
+ * (x_pitch a multiple of 8); W dense [N][K] (the nn.Linear weight), 16-byte
+ * aligned, K a multiple of 8; y rows y_pitch >= N elements apart, 2-byte
+ * aligned; only columns 0 .. N-1 of each y row are written. All pointers are
+ * device pointers borrowed for the call; the call is asynchronous on
+ * hip_stream. The result is deterministic (a fixed summation order).
+ * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE (M < 0, N < 1, K < 8, K not a multiple
+ * of 8, a pitch too small), KDA_ERR_ALIGN, KDA_ERR_HIP. M == 0 is a no-op. */
+kda_status kda_linear(const void* x, int64_t x_pitch, const void* w, void* y, int64_t y_pitch,
+                      int32_t M, int32_t N, int32_t K, void* hip_stream);
+
+/* in_proj: N = 4D + 128 + H packed outputs (D = 128 heads), K = hidden;
+ * projected rows are `pitch` elements apart (pitch >= N). */
+kda_status kda_in_proj(const void* x, int64_t x_pitch, const void* w_in, void* projected,
+                       int64_t pitch, int32_t rows, int32_t hidden, int32_t heads,
+                       void* hip_stream);
+
+/* o_proj: N = hidden, K = D = 128 heads; core rows `core_pitch` elements
+ * apart (core_pitch >= D, a multiple of 8), out rows `out_pitch` apart. */
+kda_status kda_o_proj(const void* core, int64_t core_pitch, const void* w_o, void* out,
+                      int64_t out_pitch, int32_t rows, int32_t heads, int32_t hidden,
+                      void* hip_stream);
+
 /* Number of requests skipped for an out-of-range slot or accepted count since
  * the last read. Waits for `hip_stream`, copies the counter to *count_out and
  * resets it to zero. Errors: KDA_ERR_NULL, KDA_ERR_HIP. */

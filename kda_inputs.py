@@ -175,3 +175,19 @@ def make_config(index: int) -> Case:
     name, R, L, H, num_slots, seed = (cfg.pop(k) for k in ("name", "R", "L", "H", "num_slots",
                                                            "seed"))
     return make_case(R, L, H, num_slots, seed, name=name, **cfg)
+
+
+# Projections around the core: the hidden size of the model the pages serve
+# (the back page's o_proj produces 448 x 16 = 7168 rows) and one
+# tensor-parallel rank's 12 heads.
+HIDDEN = 7168
+
+
+def make_linear(M: int, N: int, K: int, seed: int, x_pitch: Optional[int] = None):
+    """x bf16 [M, x_pitch] ~ N(0, 1) and an nn.Linear-scaled weight w bf16 [N, K]
+    ~ N(0, 1/K), drawn in that order from one generator seeded with `seed`."""
+    x_pitch = K if x_pitch is None else x_pitch
+    gen = torch.Generator().manual_seed(seed)
+    x = torch.randn(M, x_pitch, generator=gen).to(torch.bfloat16)
+    w = (torch.randn(N, K, generator=gen) * K ** -0.5).to(torch.bfloat16)
+    return x, w

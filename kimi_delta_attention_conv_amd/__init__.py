@@ -16,6 +16,7 @@ import os
 __all__ = [
     "KdaError", "KdaWeights", "KdaCaches", "load_library", "kda_prepare", "kda_decode",
     "kda_verify", "kda_device_errors", "kda_destroy", "kda_status_string", "KdaCore",
+    "kda_linear", "kda_in_proj", "kda_o_proj", "linear",
     "HEAD_DIM", "FA_RANK", "CONV_WIDTH", "MAX_TOKENS",
 ]
 
@@ -87,6 +88,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_hip_error.argtypes = []
     lib.kda_last_hip_error.restype = ctypes.c_char_p
+    lib.kda_linear.argtypes = [vp, i64, vp, vp, i64, i32, i32, i32, vp]
+    lib.kda_in_proj.argtypes = [vp, i64, vp, vp, i64, i32, i32, i32, vp]
+    lib.kda_o_proj.argtypes = [vp, i64, vp, vp, i64, i32, i32, i32, vp]
+    for f in (lib.kda_linear, lib.kda_in_proj, lib.kda_o_proj):
+        f.restype = ctypes.c_int
     # HBM stream probes (include/kda_probe.h), measurement only
     lib.kda_probe_copy.argtypes = [vp, vp, i64, vp]
     lib.kda_probe_write.argtypes = [vp, i64, ctypes.c_float, vp]
@@ -130,6 +136,48 @@ def kda_verify(handle: int, projected: int, pitch: int, requests: int, tokens: i
                slots_row_stride: int, accepted: int, core_out: int, stream: int = 0) -> None:
     _check(load_library().kda_verify(handle, projected, pitch, requests, tokens, slots,
                                      slots_row_stride, accepted, core_out, stream), "kda_verify")
+
+
+def kda_linear(x: int, x_pitch: int, w: int, y: int, y_pitch: int, M: int, N: int, K: int,
+               stream: int = 0) -> None:
+    _check(load_library().kda_linear(x, x_pitch, w, y, y_pitch, M, N, K, stream), "kda_linear")
+
+
+def kda_in_proj(x: int, x_pitch: int, w_in: int, projected: int, pitch: int, rows: int,
+                hidden: int, heads: int, stream: int = 0) -> None:
+    _check(load_library().kda_in_proj(x, x_pitch, w_in, projected, pitch, rows, hidden, heads,
+                                      stream), "kda_in_proj")
+
+
+def kda_o_proj(core: int, core_pitch: int, w_o: int, out: int, out_pitch: int, rows: int,
+               heads: int, hidden: int, stream: int = 0) -> None:
+    _check(load_library().kda_o_proj(core, core_pitch, w_o, out, out_pitch, rows, heads, hidden,
+                                     stream), "kda_o_proj")
+
+
+def _stream_of(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def linear(x, w, y=None, stream=None):
+    """y = x w^T for bf16 device tensors x [M, >=K] (unit column stride), w [N, K]
+    (dense); y [M, >=N] is allocated when not given. Returns y."""
+    import torch
+    M, N, K = x.shape[0], w.shape[0], w.shape[1]
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise TypeError("x and w must be bfloat16")
+    if x.stride(1) != 1 or not w.is_contiguous() or x.shape[1] < K:
+        raise ValueError("x needs unit column stride and >= K columns; w must be dense [N, K]")
+    if y is None:
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=x.device)
+    if y.dtype != torch.bfloat16 or y.stride(1) != 1 or y.shape[0] < M or y.shape[1] < N:
+        raise ValueError("y must be bfloat16 [>= M, >= N] with unit column stride")
+    kda_linear(x.data_ptr(), x.stride(0), w.data_ptr(), y.data_ptr(), y.stride(0), M, N, K,
+               _stream_of(stream))
+    return y
 
 
 def kda_device_errors(handle: int, stream: int = 0) -> int:

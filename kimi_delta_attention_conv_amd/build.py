@@ -16,8 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = [os.path.join(CSRC, "kda_core.hip"), os.path.join(CSRC, "kda_api.cpp"),
-           os.path.join(CSRC, "hbm_probe.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("kda_core.hip", "kda_linear.hip", "kda_api.cpp",
+                                            "hbm_probe.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

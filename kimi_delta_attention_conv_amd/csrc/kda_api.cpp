@@ -224,6 +224,44 @@ kda_status kda_verify(kda_handle h, const void* projected, int64_t pitch, int32_
     return e == hipSuccess ? KDA_OK : hip_fail(e, "kda_verify launch");
 }
 
+kda_status kda_linear(const void* x, int64_t x_pitch, const void* w, void* y, int64_t y_pitch,
+                      int32_t M, int32_t N, int32_t K, void* hip_stream) {
+    if (M < 0 || N < 1 || K < 8 || K % 8 != 0) return KDA_ERR_SHAPE;
+    if (M > (1 << 20)) return KDA_ERR_SHAPE;   // grid y limit at 64 rows a workgroup
+    if (M == 0) return KDA_OK;
+    if (x == nullptr || w == nullptr || y == nullptr) return KDA_ERR_NULL;
+    if (x_pitch < K || y_pitch < N) return KDA_ERR_SHAPE;
+    if (x_pitch % 8 != 0 || !aligned(x, 16) || !aligned(w, 16) || !aligned(y, 2))
+        return KDA_ERR_ALIGN;
+    kda::LinearParams p{};
+    p.X = static_cast<const uint16_t*>(x);
+    p.x_pitch = x_pitch;
+    p.W = static_cast<const uint16_t*>(w);
+    p.Y = static_cast<uint16_t*>(y);
+    p.y_pitch = y_pitch;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    hipError_t e = kda::launch_linear(p, static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? KDA_OK : hip_fail(e, "kda_linear launch");
+}
+
+kda_status kda_in_proj(const void* x, int64_t x_pitch, const void* w_in, void* projected,
+                       int64_t pitch, int32_t rows, int32_t hidden, int32_t heads,
+                       void* hip_stream) {
+    if (heads < 1 || heads > 4096) return KDA_ERR_SHAPE;
+    const int32_t N = 4 * heads * kda::kHeadDim + kda::kFaRank + heads;
+    return kda_linear(x, x_pitch, w_in, projected, pitch, rows, N, hidden, hip_stream);
+}
+
+kda_status kda_o_proj(const void* core, int64_t core_pitch, const void* w_o, void* out,
+                      int64_t out_pitch, int32_t rows, int32_t heads, int32_t hidden,
+                      void* hip_stream) {
+    if (heads < 1 || heads > 4096) return KDA_ERR_SHAPE;
+    return kda_linear(core, core_pitch, w_o, out, out_pitch, rows, hidden,
+                      heads * kda::kHeadDim, hip_stream);
+}
+
 kda_status kda_device_errors(kda_handle h, int32_t* count_out, void* hip_stream) {
     if (h == nullptr || count_out == nullptr) return KDA_ERR_NULL;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);

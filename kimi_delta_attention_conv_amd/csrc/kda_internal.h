@@ -63,7 +63,18 @@ struct PrepareParams {
     int32_t heads;
 };
 
+// Y[M][N] = X[M][K] W[N][K]^T (bf16 in, fp32 accumulate, bf16 out).
+struct LinearParams {
+    const uint16_t* X;   // rows x_pitch elements apart, 16-byte aligned
+    int64_t x_pitch;
+    const uint16_t* W;   // dense [N][K]
+    uint16_t* Y;         // rows y_pitch elements apart
+    int64_t y_pitch;
+    int32_t M, N, K;     // K a multiple of 8
+};
+
 hipError_t launch_prepare(const PrepareParams& in, const PreparedWeights& out, hipStream_t s);
+hipError_t launch_linear(const LinearParams& p, hipStream_t s);
 hipError_t launch_core(int tokens, const CoreParams& p, hipStream_t s);
 
 }  // namespace kda

@@ -88,6 +88,11 @@ class Oracle:
         lib.kda_ref_gated_rmsnorm.restype = None
         lib.kda_ref_run.argtypes = [ctypes.POINTER(Problem)]
         lib.kda_ref_run.restype = i32
+        i64 = ctypes.c_int64
+        lib.kda_ref_linear.argtypes = [i32, i32, i32, p, i64, p, p, i64, p]
+        lib.kda_ref_linear.restype = None
+        lib.kda_ref_linear_entries.argtypes = [i32, p, i64, p, i32, p, p, p]
+        lib.kda_ref_linear_entries.restype = None
         self.lib = lib
         self.path = path
 
@@ -149,6 +154,32 @@ class Oracle:
         self.lib.kda_ref_gated_rmsnorm(o.size, _ptr(o), _ptr(gate_raw), _ptr(w), float(eps),
                                        _ptr(y))
         return y
+
+    # ------------------------------------------------------------ projections
+    def linear(self, x_bits, w_bits, x_pitch=None, with_f64=True):
+        """y = x w^T for bf16 bit patterns x [M][>=K] (rows x_pitch apart) and
+        w [N][K]. Returns (y bf16 bits [M][N], y float64 [M][N] or None)."""
+        x_bits, w_bits = _u16(x_bits), _u16(w_bits)
+        N, K = w_bits.shape
+        M = x_bits.shape[0]
+        x_pitch = x_bits.shape[1] if x_pitch is None else x_pitch
+        y = np.zeros((M, N), np.uint16)
+        y64 = np.zeros((M, N), np.float64) if with_f64 else None
+        self.lib.kda_ref_linear(M, N, K, _ptr(x_bits), x_pitch, _ptr(w_bits), _ptr(y), N,
+                                _ptr(y64))
+        return y, y64
+
+    def linear_entries(self, x_bits, w_bits, ms, ns, x_pitch=None):
+        """Entries (ms[i], ns[i]) of x w^T in float64."""
+        x_bits, w_bits = _u16(x_bits), _u16(w_bits)
+        K = w_bits.shape[1]
+        x_pitch = x_bits.shape[1] if x_pitch is None else x_pitch
+        ms = np.ascontiguousarray(ms, dtype=np.int32)
+        ns = np.ascontiguousarray(ns, dtype=np.int32)
+        out = np.zeros(ms.size, np.float64)
+        self.lib.kda_ref_linear_entries(K, _ptr(x_bits), x_pitch, _ptr(w_bits), ms.size,
+                                        _ptr(ms), _ptr(ns), _ptr(out))
+        return out
 
     # ------------------------------------------------------------ whole call
     def run(self, *, heads, width, requests, tokens, projected, pitch, slots, slots_row_stride,

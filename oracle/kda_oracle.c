@@ -339,3 +339,46 @@ int32_t kda_ref_run(const kda_ref_problem* p)
     free(y); free(g); free(qh); free(kh); free(o); free(gate); free(yo); free(dst);
     return skipped;
 }
+
+/* ---------------------------------------------------------------------- */
+/* Projections around the core (in_proj before it, o_proj after it)       */
+/* ---------------------------------------------------------------------- */
+
+/* y[m][n] = sum_k x[m][k] * w[n][k] for the rows of `rows` (or all M rows
+ * when rows == NULL), in double, k ascending; the nn.Linear weight layout
+ * [N][K] ([kda] module docstring, gemv role: in_proj -> q|k|v|g|f_a|beta;
+ * page "vllm.models.kimi_k3.amd.specialized_decode.mono.attention.back",
+ * module docstring: o_proj with K = 1536 local). x rows are x_pitch apart,
+ * y rows y_pitch apart; y gets bf16 (round to nearest even from double) and,
+ * when y_f64 is not NULL, the unrounded value (y_f64 rows are N apart). */
+void kda_ref_linear(int32_t M, int32_t N, int32_t K, const uint16_t* x, int64_t x_pitch,
+                    const uint16_t* w, uint16_t* y, int64_t y_pitch, double* y_f64)
+{
+    double* xr = malloc(sizeof(double) * (size_t)K);
+    for (int32_t m = 0; m < M; ++m) {
+        for (int32_t k = 0; k < K; ++k) xr[k] = kda_ref_bf16_to_double(x[(int64_t)m * x_pitch + k]);
+        for (int32_t n = 0; n < N; ++n) {
+            const uint16_t* wr = w + (int64_t)n * K;
+            double acc = 0.0;
+            for (int32_t k = 0; k < K; ++k) acc += xr[k] * kda_ref_bf16_to_double(wr[k]);
+            y[(int64_t)m * y_pitch + n] = kda_ref_double_to_bf16(acc);
+            if (y_f64) y_f64[(int64_t)m * N + n] = acc;
+        }
+    }
+    free(xr);
+}
+
+/* The same contraction for a list of (m, n) entries only (sampled checks at
+ * full size): out[i] = sum_k x[ms[i]][k] * w[ns[i]][k], in double. */
+void kda_ref_linear_entries(int32_t K, const uint16_t* x, int64_t x_pitch, const uint16_t* w,
+                            int32_t count, const int32_t* ms, const int32_t* ns, double* out)
+{
+    for (int32_t i = 0; i < count; ++i) {
+        const uint16_t* xr = x + (int64_t)ms[i] * x_pitch;
+        const uint16_t* wr = w + (int64_t)ns[i] * K;
+        double acc = 0.0;
+        for (int32_t k = 0; k < K; ++k)
+            acc += kda_ref_bf16_to_double(xr[k]) * kda_ref_bf16_to_double(wr[k]);
+        out[i] = acc;
+    }
+}

@@ -478,3 +478,35 @@ def check_call_state_stays_bounded(orc):
         vmax = max(vmax, float(np.abs(res["state"]).max()))
         assert np.all(np.isfinite(res["out_f64"]))
     assert vmax < 50.0, vmax
+
+
+# ----------------------------------------------------------------- projections
+
+def _bf16_bits(rng, shape, scale=1.0):
+    f = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pin
+def check_linear_against_numpy_and_closed_forms(orc):
+    """y = x W^T: numpy float64 matmul on the widened inputs; an identity block
+    copies columns exactly; one-hot rows of x pick columns of W exactly; the
+    entry-wise form equals the full one; x rows may be padded (pitch > K)."""
+    rng = np.random.default_rng(31)
+    M, N, K, pitch = 5, 9, 48, 56
+    x = _bf16_bits(rng, (M, pitch))
+    w = _bf16_bits(rng, (N, K), 0.2)
+    y, y64 = orc.linear(x, w, x_pitch=pitch)
+    ref = om.bf16_bits_to_f64(x[:, :K]) @ om.bf16_bits_to_f64(w).T
+    _close(y64, ref, 1e-12, 1e-14, "linear vs numpy")
+    assert np.array_equal(y, orc.f64_to_bf16_bits(y64)), "bf16 output is the RNE of the sum"
+    eye = np.zeros((N, K), np.uint16)
+    eye[np.arange(N), np.arange(N)] = 0x3F80                  # 1.0 in bf16
+    y_eye, _ = orc.linear(x, eye, x_pitch=pitch)
+    assert np.array_equal(y_eye, x[:, :N])
+    onehot = np.zeros((K, K), np.uint16)
+    onehot[np.arange(K), np.arange(K)] = 0x3F80
+    y_oh, _ = orc.linear(onehot, w)
+    assert np.array_equal(y_oh, w.T)
+    ms, ns = rng.integers(0, M, 20), rng.integers(0, N, 20)
+    _close(orc.linear_entries(x, w, ms, ns, x_pitch=pitch), y64[ms, ns], 0, 0, "entries")

@@ -1,0 +1,120 @@
+"""The projection kernel (kda_linear / kda_in_proj / kda_o_proj) vs the oracle.
+
+Bar (derived from the arithmetic): bf16 x bf16 products are exact in fp32, so
+the kernel's only error before the output rounding is fp32 accumulation, at
+most K 2^-24 sum_k |x_k w_k|; the bf16 output adds at most half an ulp, 2^-9
+|y|. Each element must satisfy |y_gpu - y| <= 2^-8 |y| + K 2^-24 sum|x w| with
+y the oracle's double-precision value. Untouched output columns (pitch > N)
+must stay bit-exact, and two runs must agree bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kda_inputs import HIDDEN, make_linear
+from oracle_cases import bf16_np
+
+pytestmark = pytest.mark.gpu
+
+SENT = 0x7FC1
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _run(x, w, y_pitch=None, M=None, fn="linear", heads=None):
+    import kimi_delta_attention_conv_amd as kda
+    M = x.shape[0] if M is None else M
+    N, K = w.shape
+    y_pitch = N if y_pitch is None else y_pitch
+    xd, wd = x.cuda(), w.cuda()
+    y = torch.full((max(M, 1), y_pitch), SENT, dtype=torch.int16).view(torch.bfloat16).cuda()
+    s = torch.cuda.current_stream().cuda_stream
+    if fn == "linear":
+        kda.kda_linear(xd.data_ptr(), xd.stride(0), wd.data_ptr(), y.data_ptr(), y_pitch, M, N, K, s)
+    elif fn == "in_proj":
+        kda.kda_in_proj(xd.data_ptr(), xd.stride(0), wd.data_ptr(), y.data_ptr(), y_pitch, M, K,
+                        heads, s)
+    else:
+        kda.kda_o_proj(xd.data_ptr(), xd.stride(0), wd.data_ptr(), y.data_ptr(), y_pitch, M,
+                       heads, N, s)
+    torch.cuda.synchronize()
+    return bf16_np(y.cpu())
+
+
+def _check(x, w, got, ms=None, ns=None, label=""):
+    orc = oracle.default()
+    xb, wb = bf16_np(x), bf16_np(w)
+    N, K = wb.shape
+    M = xb.shape[0]
+    if ms is None:
+        _, ref = orc.linear(xb, wb)
+        ms, ns = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        ms, ns = ms.ravel(), ns.ravel()
+        ref = ref.ravel()
+    else:
+        ref = orc.linear_entries(xb, wb, ms, ns)
+    xf = oracle.bf16_bits_to_f64(xb[:, :K])
+    wf = oracle.bf16_bits_to_f64(wb)
+    absdot = np.einsum("ik,ik->i", np.abs(xf[ms]), np.abs(wf[ns]))
+    g = (got[ms, ns].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    err = np.abs(g - ref)
+    lim = 2.0 ** -8 * np.abs(ref) + K * 2.0 ** -24 * absdot
+    assert np.all(np.isfinite(g)), label
+    worst = float(np.max(err / np.maximum(lim, 1e-300)))
+    print(f"[linear] {label}: {ms.size} entries, max err/limit {worst:.3f}, "
+          f"max abs err {err.max():.3e}", flush=True)
+    assert worst <= 1.0, label
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 8), (5, 37, 136), (16, 16, 128), (17, 33, 264),
+                                   (33, 100, 1024), (64, 48, 520), (70, 129, 384)])
+def test_ragged_shapes(M, N, K):
+    x, w = make_linear(M, N, K, seed=M * 1000 + N + K, x_pitch=K + 8)
+    got = _run(x, w, y_pitch=N + 3)
+    _check(x, w, got[:, :N], label=f"M={M} N={N} K={K}")
+    assert np.all(got[:, N:] == SENT), "columns beyond N were written"
+
+
+@pytest.mark.parametrize("rows", [64, 512])
+def test_in_proj_full_shape(rows):
+    heads = 12
+    N = 4 * 128 * heads + 128 + heads
+    x, w = make_linear(rows, N, HIDDEN, seed=rows)
+    got = _run(x, w, fn="in_proj", heads=heads)
+    rng = np.random.default_rng(rows)
+    ms, ns = rng.integers(0, rows, 3000), rng.integers(0, N, 3000)
+    _check(x, w, got, ms, ns, label=f"in_proj rows={rows}")
+    again = _run(x, w, fn="in_proj", heads=heads)
+    assert np.array_equal(got, again), "not deterministic"
+
+
+@pytest.mark.parametrize("rows", [64, 512])
+def test_o_proj_full_shape(rows):
+    heads = 12
+    x, w = make_linear(rows, HIDDEN, 128 * heads, seed=10 + rows)
+    got = _run(x, w, fn="o_proj", heads=heads)
+    rng = np.random.default_rng(rows + 1)
+    ms, ns = rng.integers(0, rows, 3000), rng.integers(0, HIDDEN, 3000)
+    _check(x, w, got, ms, ns, label=f"o_proj rows={rows}")
+
+
+def test_validation():
+    import kimi_delta_attention_conv_amd as kda
+    x, w = make_linear(4, 16, 64, seed=5)
+    xd, wd = x.cuda(), w.cuda()
+    y = torch.zeros(4, 16, dtype=torch.bfloat16, device="cuda")
+    for args, status in [((xd.data_ptr(), 64, wd.data_ptr(), y.data_ptr(), 16, 4, 16, 60), -2),
+                         ((xd.data_ptr(), 60, wd.data_ptr(), y.data_ptr(), 16, 4, 16, 64), -2),
+                         ((xd.data_ptr() + 8, 64, wd.data_ptr(), y.data_ptr(), 16, 4, 16, 64), -3),
+                         ((0, 64, wd.data_ptr(), y.data_ptr(), 16, 4, 16, 64), -1),
+                         ((xd.data_ptr(), 64, wd.data_ptr(), y.data_ptr(), 8, 4, 16, 64), -2)]:
+        with pytest.raises(kda.KdaError) as ei:
+            kda.kda_linear(*args)
+        assert ei.value.status == status
+    kda.kda_linear(0, 64, 0, 0, 16, 0, 16, 64)   # M == 0: no-op
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)

@@ -46,6 +46,12 @@ MUTATIONS = {
     "bf16_truncates": ("double r = nearbyint(a / q) * q;", "double r = floor(a / q) * q;"),
     "gate_reads_gate_columns": ("kda_ref_gate(H, fb, x + 4 * (int64_t)D,",
                                 "kda_ref_gate(H, fb, x + 3 * (int64_t)D,"),
+    "linear_drops_last_k": ("for (int32_t k = 0; k < K; ++k) acc += xr[k] * kda_ref_bf16_to_double(wr[k]);",
+                            "for (int32_t k = 0; k + 1 < K; ++k) acc += xr[k] * kda_ref_bf16_to_double(wr[k]);"),
+    "linear_weight_transposed": ("const uint16_t* wr = w + (int64_t)n * K;\n            double acc",
+                                 "const uint16_t* wr = w + (int64_t)n;\n            double acc"),
+    "linear_ignores_pitch": ("for (int32_t k = 0; k < K; ++k) xr[k] = kda_ref_bf16_to_double(x[(int64_t)m * x_pitch + k]);",
+                             "for (int32_t k = 0; k < K; ++k) xr[k] = kda_ref_bf16_to_double(x[(int64_t)m * K + k]);"),
 }
 
 
