@@ -9,16 +9,19 @@
 //   docstring and stage_o: o_proj over the core rows (K = 1536 local), an
 //   MFMA GEMV with the token dimension padded to 16.
 //
-// Both operands are K-contiguous (rows of X, rows of the nn.Linear weight W),
-// so every lane reads 64 contiguous bytes of one row per 128-wide K block and
-// feeds v_mfma_f32_16x16x32_bf16 directly from registers. Within a K block,
-// lane group kg (= lane >> 4) owns K elements 32kg .. 32kg + 31 and hands
-// 8 of them to each of the 4 MFMA K steps; A and B use the same assignment,
-// so the product is unchanged.
+// Two kernels, chosen by the row count M:
 //
-// A workgroup computes 16 output columns for 16 * MT rows; its 4 waves take
+// Skinny (M <= 64, decode-sized): both operands are K-contiguous (rows of X,
+// rows of the nn.Linear weight W), so every lane reads 64 contiguous bytes of
+// one row per 128-wide K block and feeds v_mfma_f32_16x16x32_bf16 directly
+// from registers. Within a K block, lane group kg (= lane >> 4) owns K
+// elements 32kg .. 32kg + 31 and hands 8 of them to each of the 4 MFMA K
+// steps; A and B use the same assignment, so the product is unchanged. A
+// workgroup computes 16 * NT output columns for 16 * MT rows; its waves take
 // the K blocks round-robin and their partial tiles are summed through LDS in
 // wave order (a fixed order: results do not depend on timing).
+//
+// Tiled (M > 64): BM x BN tiles with X and W blocks staged through LDS.
 #include "kda_internal.h"
 
 namespace kda {
@@ -28,8 +31,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kLinWaves = 4;
-constexpr int kLinThreads = 64 * kLinWaves;
 constexpr int kKBlock = 128;
 
 __device__ __forceinline__ bf16x8 load8(const uint16_t* p, bool ok) {
@@ -41,19 +42,24 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-template <int MT>
-__global__ __launch_bounds__(kLinThreads) void linear_skinny_kernel(const LinearParams p) {
-    const int n0 = blockIdx.x * 16;
+template <int MT, int NT, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void linear_skinny_kernel(const LinearParams p) {
+    const int n0 = blockIdx.x * (16 * NT);
     const int m0 = blockIdx.y * (16 * MT);
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int mn = lane & 15;   // B column (output n) / A row (token m) of this lane
     const int kg = lane >> 4;   // which 32-wide slice of each K block
 
-    // out-of-range rows read a valid row and are zeroed
-    const int n = n0 + mn;
-    const bool n_ok = n < p.N;
-    const uint16_t* wrow = p.W + (int64_t)(n_ok ? n : p.N - 1) * p.K;
+    // out-of-range rows read nothing and are zero
+    const uint16_t* wrow[NT];
+    bool n_ok[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int n = n0 + 16 * j + mn;
+        n_ok[j] = n < p.N;
+        wrow[j] = p.W + (int64_t)(n_ok[j] ? n : p.N - 1) * p.K;
+    }
     const uint16_t* xrow[MT];
     bool m_ok[MT];
 #pragma unroll
@@ -63,60 +69,207 @@ __global__ __launch_bounds__(kLinThreads) void linear_skinny_kernel(const Linear
         xrow[i] = p.X + (int64_t)(m_ok[i] ? m : p.M - 1) * p.x_pitch;
     }
 
-    f32x4 acc[MT];
+    f32x4 acc[MT][NT];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int nkb = (p.K + kKBlock - 1) / kKBlock;
-    for (int kb = wave; kb < nkb; kb += kLinWaves) {
+    for (int kb = wave; kb < nkb; kb += WAVES) {
         const int kbase = kb * kKBlock + 32 * kg;
-        bf16x8 b[4];
+        bf16x8 b[NT][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = load8(wrow + kbase + 8 * j, n_ok && kbase + 8 * j + 8 <= p.K);
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                b[j][q] = load8(wrow[j] + kbase + 8 * q, n_ok[j] && kbase + 8 * q + 8 <= p.K);
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             bf16x8 a[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                a[j] = load8(xrow[i] + kbase + 8 * j, m_ok[i] && kbase + 8 * j + 8 <= p.K);
+            for (int q = 0; q < 4; ++q)
+                a[q] = load8(xrow[i] + kbase + 8 * q, m_ok[i] && kbase + 8 * q + 8 <= p.K);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j], acc[i], 0, 0, 0);
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q], b[j][q], acc[i][j], 0, 0, 0);
         }
     }
 
-    // sum the 4 waves' partial tiles in wave order; lane holds rows 4 kg + r
-    // (r = 0..3) of each 16-row tile, column mn
-    __shared__ float red[kLinWaves][MT * 4][64];
+    // sum the waves' partial tiles in wave order; lane holds rows 4 kg + r
+    // (r = 0..3) of each 16-row tile, column mn of each 16-column tile
+    __shared__ float red[WAVES][MT * NT * 4][64];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][i * 4 + r][lane] = acc[i][r];
-    __syncthreads();
-    for (int e = threadIdx.x; e < MT * 4 * 64; e += kLinThreads) {
-        const int ir = e >> 6, l = e & 63;
-        float s = red[0][ir][l];
+        for (int j = 0; j < NT; ++j)
 #pragma unroll
-        for (int w = 1; w < kLinWaves; ++w) s += red[w][ir][l];
-        const int m = m0 + 16 * (ir >> 2) + 4 * (l >> 4) + (ir & 3);
-        const int nn = n0 + (l & 15);
+            for (int r = 0; r < 4; ++r) red[wave][(i * NT + j) * 4 + r][lane] = acc[i][j][r];
+    __syncthreads();
+    for (int e = threadIdx.x; e < MT * NT * 4 * 64; e += 64 * WAVES) {
+        const int ijr = e >> 6, l = e & 63;
+        float s = red[0][ijr][l];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) s += red[w][ijr][l];
+        const int i = (ijr >> 2) / NT, j = (ijr >> 2) % NT;
+        const int m = m0 + 16 * i + 4 * (l >> 4) + (ijr & 3);
+        const int nn = n0 + 16 * j + (l & 15);
         if (m < p.M && nn < p.N) p.Y[(int64_t)m * p.y_pitch + nn] = to_bf16(s);
     }
 }
 
-template <int MT>
-hipError_t launch_t(const LinearParams& p, hipStream_t s) {
-    const dim3 grid((unsigned)((p.N + 15) / 16), (unsigned)((p.M + 16 * MT - 1) / (16 * MT)));
-    hipLaunchKernelGGL(linear_skinny_kernel<MT>, grid, dim3(kLinThreads), 0, s, p);
+// Tiled kernel for larger M: a workgroup of 4 waves computes a BM x BN tile
+// (waves 2 x 2, each (BM/2) x (BN/2) as 16 x 16 MFMA tiles). K advances in
+// blocks of 64: each block of X and W rows is staged through LDS (rows padded
+// by 16 bytes) and the next block's global loads are in flight while the
+// current one is multiplied, with one barrier per block.
+constexpr int kTileK = 64;
+constexpr int kLdsRow = kTileK + 8;   // elements; 144-byte rows
+
+template <int BM, int BN, int DEPTH>
+__global__ __launch_bounds__(256) void linear_tiled_kernel(const LinearParams p) {
+    constexpr int TM = BM / 32;            // 16-row tiles per wave
+    constexpr int TN = BN / 32;            // 16-column tiles per wave
+    constexpr int A_LD = BM * 8 / 256;     // 16-byte pieces of the X block per thread
+    constexpr int B_LD = BN * 8 / 256;     // 16-byte pieces of the W block per thread
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM][kLdsRow];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN][kLdsRow];
+
+    // XCD-aware tile order: workgroup g runs on XCD g % 8; XCD x takes a
+    // contiguous range of tiles, M-blocks of one N-block adjacent, so the
+    // workgroups that share a W slab (and the X rows) meet in one XCD's L2.
+    const int mblocks = (p.M + BM - 1) / BM;
+    const int tiles = mblocks * ((p.N + BN - 1) / BN);
+    int t = blockIdx.x;
+    {
+        const int q = tiles >> 3;
+        if ((int)blockIdx.x < 8 * q) t = (blockIdx.x & 7) * q + (blockIdx.x >> 3);
+    }
+    const int m0 = (t % mblocks) * BM;
+    const int n0 = (t / mblocks) * BN;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int mn = lane & 15, kg = lane >> 4;
+
+    // Register stages of the global -> LDS copy: stage d holds K block kb with
+    // kb % DEPTH == d, so DEPTH - 1 blocks are in flight while one is
+    // multiplied. Piece q of a thread covers row (tid * A_LD + q) / 8 of the
+    // block and its K elements 8 * ((tid * A_LD + q) % 8) .. +8.
+    u32x4 ra[DEPTH][A_LD], rb[DEPTH][B_LD];
+    const int nkb = (p.K + kTileK - 1) / kTileK;
+    auto gload = [&](u32x4 (&a)[A_LD], u32x4 (&b)[B_LD], int kb) {
+#pragma unroll
+        for (int q = 0; q < A_LD; ++q) {
+            const int piece = tid * A_LD + q, row = piece >> 3, k = kb * kTileK + 8 * (piece & 7);
+            const int m = m0 + row;
+            const bool ok = kb < nkb && m < p.M && k + 8 <= p.K;
+            a[q] = ok ? *reinterpret_cast<const u32x4*>(p.X + (int64_t)m * p.x_pitch + k)
+                      : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int q = 0; q < B_LD; ++q) {
+            const int piece = tid * B_LD + q, row = piece >> 3, k = kb * kTileK + 8 * (piece & 7);
+            const int n = n0 + row;
+            const bool ok = kb < nkb && n < p.N && k + 8 <= p.K;
+            b[q] = ok ? *reinterpret_cast<const u32x4*>(p.W + (int64_t)n * p.K + k)
+                      : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto lstore = [&](const u32x4 (&a)[A_LD], const u32x4 (&b)[B_LD], int buf) {
+#pragma unroll
+        for (int q = 0; q < A_LD; ++q) {
+            const int piece = tid * A_LD + q;
+            *reinterpret_cast<u32x4*>(&sA[buf][piece >> 3][8 * (piece & 7)]) = a[q];
+        }
+#pragma unroll
+        for (int q = 0; q < B_LD; ++q) {
+            const int piece = tid * B_LD + q;
+            *reinterpret_cast<u32x4*>(&sB[buf][piece >> 3][8 * (piece & 7)]) = b[q];
+        }
+    };
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) gload(ra[d], rb[d], d);
+    lstore(ra[0], rb[0], 0);
+    __syncthreads();
+    for (int base = 0; base < nkb; base += DEPTH) {
+#pragma unroll
+        for (int u = 0; u < DEPTH; ++u) {
+            const int kb = base + u;
+            if (kb >= nkb) break;
+            const int buf = kb & 1;
+            // stage u held block kb (now in LDS): refill it with block kb + DEPTH
+            gload(ra[u], rb[u], kb + DEPTH);
+#pragma unroll
+            for (int s = 0; s < kTileK / 32; ++s) {
+                bf16x8 a[TM], b[TN];
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                        &sA[buf][wm * (BM / 2) + 16 * i + mn][32 * s + 8 * kg]));
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                        &sB[buf][wn * (BN / 2) + 16 * j + mn][32 * s + 8 * kg]));
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            }
+            if (kb + 1 < nkb) lstore(ra[(u + 1) % DEPTH], rb[(u + 1) % DEPTH], buf ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // lane holds rows 4 kg + r (r = 0..3) of each 16-row tile, column mn
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = n0 + wn * (BN / 2) + 16 * j + mn;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + wm * (BM / 2) + 16 * i + 4 * kg + r;
+                if (m < p.M && n < p.N) p.Y[(int64_t)m * p.y_pitch + n] = to_bf16(acc[i][j][r]);
+            }
+        }
+}
+
+template <int MT, int NT, int WAVES>
+hipError_t launch_skinny(const LinearParams& p, hipStream_t s) {
+    const dim3 grid((unsigned)((p.N + 16 * NT - 1) / (16 * NT)), (unsigned)((p.M + 16 * MT - 1) / (16 * MT)));
+    hipLaunchKernelGGL((linear_skinny_kernel<MT, NT, WAVES>), grid, dim3(64 * WAVES), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int DEPTH>
+hipError_t launch_tiled(const LinearParams& p, hipStream_t s) {
+    const int64_t tiles = (int64_t)((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
+    hipLaunchKernelGGL((linear_tiled_kernel<BM, BN, DEPTH>), dim3((unsigned)tiles), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_linear(const LinearParams& p, hipStream_t s) {
-    if (p.M <= 16) return launch_t<1>(p, s);
-    if (p.M <= 32) return launch_t<2>(p, s);
-    return launch_t<4>(p, s);
+    // shapes measured on MI355X at the projections' sizes (7168 -> 6284,
+    // 1536 -> 7168): 2 column tiles a wave and 8 waves for up to 64 rows,
+    // 128 x 64 LDS tiles above
+    if (p.M <= 16) return launch_skinny<1, 2, 8>(p, s);
+    if (p.M <= 32) return launch_skinny<2, 2, 8>(p, s);
+    if (p.M <= 64) return launch_skinny<4, 2, 8>(p, s);
+    return launch_tiled<128, 64, 1>(p, s);
 }
 
 }  // namespace kda
