@@ -14,9 +14,9 @@
 // Skinny (M <= 64, decode-sized): both operands are K-contiguous (rows of X,
 // rows of the nn.Linear weight W), so every lane reads 64 contiguous bytes of
 // one row per 128-wide K block and feeds v_mfma_f32_16x16x32_bf16 directly
-// from registers. Within a K block, lane group kg (= lane >> 4) owns K
-// elements 32kg .. 32kg + 31 and hands 8 of them to each of the 4 MFMA K
-// steps; A and B use the same assignment, so the product is unchanged. A
+// from registers. Within a K block, lane group kg (= lane >> 4) hands K
+// elements 8 (kg + 4q) .. +8 to MFMA K step q; A and B use the same
+// assignment, so the product is unchanged. A
 // workgroup computes 16 * NT output columns for 16 * MT rows; its waves take
 // the K blocks round-robin and their partial tiles are summed through LDS in
 // wave order (a fixed order: results do not depend on timing).
@@ -77,19 +77,21 @@ __global__ __launch_bounds__(64 * WAVES) void linear_skinny_kernel(const LinearP
 
     const int nkb = (p.K + kKBlock - 1) / kKBlock;
     for (int kb = wave; kb < nkb; kb += WAVES) {
-        const int kbase = kb * kKBlock + 32 * kg;
+        // K step q of this lane uses elements 8 (kg + 4q) .. +8 of the block:
+        // the 4 lanes of a row read 64 contiguous bytes per load instruction
+        const int kbase = kb * kKBlock + 8 * kg;
         bf16x8 b[NT][4];
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                b[j][q] = load8(wrow[j] + kbase + 8 * q, n_ok[j] && kbase + 8 * q + 8 <= p.K);
+                b[j][q] = load8(wrow[j] + kbase + 32 * q, n_ok[j] && kbase + 32 * q + 8 <= p.K);
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             bf16x8 a[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                a[q] = load8(xrow[i] + kbase + 8 * q, m_ok[i] && kbase + 8 * q + 8 <= p.K);
+                a[q] = load8(xrow[i] + kbase + 32 * q, m_ok[i] && kbase + 32 * q + 8 <= p.K);
 #pragma unroll
             for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -157,14 +159,15 @@ __global__ __launch_bounds__(256) void linear_tiled_kernel(const LinearParams p)
 
     // Register stages of the global -> LDS copy: stage d holds K block kb with
     // kb % DEPTH == d, so DEPTH - 1 blocks are in flight while one is
-    // multiplied. Piece q of a thread covers row (tid * A_LD + q) / 8 of the
-    // block and its K elements 8 * ((tid * A_LD + q) % 8) .. +8.
+    // multiplied. Piece q of a thread is piece q * 256 + tid of the block:
+    // row piece / 8, K elements 8 * (piece % 8) .. +8, so 8 consecutive lanes
+    // read one 128-byte row segment.
     u32x4 ra[DEPTH][A_LD], rb[DEPTH][B_LD];
     const int nkb = (p.K + kTileK - 1) / kTileK;
     auto gload = [&](u32x4 (&a)[A_LD], u32x4 (&b)[B_LD], int kb) {
 #pragma unroll
         for (int q = 0; q < A_LD; ++q) {
-            const int piece = tid * A_LD + q, row = piece >> 3, k = kb * kTileK + 8 * (piece & 7);
+            const int piece = q * 256 + tid, row = piece >> 3, k = kb * kTileK + 8 * (piece & 7);
             const int m = m0 + row;
             const bool ok = kb < nkb && m < p.M && k + 8 <= p.K;
             a[q] = ok ? *reinterpret_cast<const u32x4*>(p.X + (int64_t)m * p.x_pitch + k)
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(256) void linear_tiled_kernel(const LinearParams p)
         }
 #pragma unroll
         for (int q = 0; q < B_LD; ++q) {
-            const int piece = tid * B_LD + q, row = piece >> 3, k = kb * kTileK + 8 * (piece & 7);
+            const int piece = q * 256 + tid, row = piece >> 3, k = kb * kTileK + 8 * (piece & 7);
             const int n = n0 + row;
             const bool ok = kb < nkb && n < p.N && k + 8 <= p.K;
             b[q] = ok ? *reinterpret_cast<const u32x4*>(p.W + (int64_t)n * p.K + k)
@@ -182,12 +185,12 @@ __global__ __launch_bounds__(256) void linear_tiled_kernel(const LinearParams p)
     auto lstore = [&](const u32x4 (&a)[A_LD], const u32x4 (&b)[B_LD], int buf) {
 #pragma unroll
         for (int q = 0; q < A_LD; ++q) {
-            const int piece = tid * A_LD + q;
+            const int piece = q * 256 + tid;
             *reinterpret_cast<u32x4*>(&sA[buf][piece >> 3][8 * (piece & 7)]) = a[q];
         }
 #pragma unroll
         for (int q = 0; q < B_LD; ++q) {
-            const int piece = tid * B_LD + q;
+            const int piece = q * 256 + tid;
             *reinterpret_cast<u32x4*>(&sB[buf][piece >> 3][8 * (piece & 7)]) = b[q];
         }
     };
