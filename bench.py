@@ -52,6 +52,9 @@ def parse_args():
     ap.add_argument("--probe", action="store_true", help="also run the HBM probes")
     ap.add_argument("--probe-only", action="store_true",
                     help="run only the HBM probes (counter calibration)")
+    ap.add_argument("--graph", type=int, default=0, metavar="CHAIN",
+                    help="capture CHAIN consecutive launches (rotating slot sets) in one HIP "
+                         "graph and time graph replays (steps rounded up to whole replays)")
     ap.add_argument("--proj", action="store_true",
                     help="time the in_proj / o_proj projections at the workload's row count "
                          "instead of the core (prints one JSON line)")
@@ -256,18 +259,33 @@ def main():
     slot_base = slot_base.to(dev)
     sets = [torch.as_strided(slot_base, shape, stride, off) for shape, stride, off in views]
     accepted = None if case.accepted is None else case.accepted.to(dev)
-    stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
     h = core.handle
     pitch = case.pitch
     lib = kda.load_library()
-    if accepted is None:
-        launches = [(lambda s=s: lib.kda_decode(h, projected.data_ptr(), pitch, case.R,
-                                                s.data_ptr(), out.data_ptr(), sp)) for s in sets]
-    else:
-        launches = [(lambda s=s: lib.kda_verify(h, projected.data_ptr(), pitch, case.R, case.L,
-                                                s.data_ptr(), s.stride(0), accepted.data_ptr(),
-                                                out.data_ptr(), sp)) for s in sets]
+
+    def make_launch(s, sp):
+        if accepted is None:
+            return lambda: lib.kda_decode(h, projected.data_ptr(), pitch, case.R, s.data_ptr(),
+                                          out.data_ptr(), sp)
+        return lambda: lib.kda_verify(h, projected.data_ptr(), pitch, case.R, case.L,
+                                      s.data_ptr(), s.stride(0), accepted.data_ptr(),
+                                      out.data_ptr(), sp)
+
+    stream = torch.cuda.current_stream()
+    launches = [make_launch(s, stream.cuda_stream) for s in sets]
+    if args.graph:
+        chain = args.graph
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            sp_cap = torch.cuda.current_stream().cuda_stream
+            for i in range(chain):
+                rc = make_launch(sets[i % len(sets)], sp_cap)()
+                if rc != 0:
+                    raise RuntimeError(f"capture failed: {kda.kda_status_string(rc)}")
+        args.warmup = -(-args.warmup // chain)
+        args.steps = -(-args.steps // chain)
+        launches = [lambda: (graph.replay(), 0)[1]]
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
@@ -292,8 +310,10 @@ def main():
     if errors:
         raise RuntimeError(f"{errors} requests were skipped for invalid slots")
 
-    ms_per_step = wall * 1e3 / args.steps
-    kernel_ms = gpu_ms / args.steps          # one launch of the core kernel per step
+    per_replay = args.graph if args.graph else 1
+    steps_run = args.steps * per_replay
+    ms_per_step = wall * 1e3 / steps_run
+    kernel_ms = gpu_ms / steps_run           # one launch of the core kernel per step
     metric_bytes = (case.R + case.S) * case.H * UNIT_BYTES
     achieved = metric_bytes / (kernel_ms * 1e-3) / 1e9
     traffic = None
@@ -306,8 +326,8 @@ def main():
         "value": round(case.S / (ms_per_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps_run,
+        "warmup": args.warmup * per_replay,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -317,7 +337,8 @@ def main():
         "config": {"workload": case.name, "requests": case.R, "tokens": case.L,
                    "rows": case.S, "heads": case.H, "head_dim": 128, "pool_slots": case.num_slots,
                    "conv_layout": "dim_first" if case.conv_dim_first else "transposed",
-                   "slot_sets_rotated": len(sets), "io": "bf16", "state": "f32"},
+                   "slot_sets_rotated": len(sets), "io": "bf16", "state": "f32",
+                   "launch": f"hip_graph x{args.graph}" if args.graph else "eager"},
         "gbps": round(metric_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "metric_bytes_per_step": metric_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
