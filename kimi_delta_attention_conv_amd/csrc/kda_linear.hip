@@ -21,7 +21,8 @@
 // the K blocks round-robin and their partial tiles are summed through LDS in
 // wave order (a fixed order: results do not depend on timing).
 //
-// Tiled (M > 64): BM x BN tiles with X and W blocks staged through LDS.
+// Tiled (M > 64): BM x BN tiles with X and W blocks staged through LDS and
+// the next blocks' global loads in flight in register stages.
 #include "kda_internal.h"
 
 namespace kda {
@@ -33,6 +34,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kKBlock = 128;
 
+// 16 bytes, or zero without a load when `ok` is false. (The skinny kernel
+// measured faster with this guarded form than with clamped unconditional
+// loads; the tiled kernel below loads unconditionally instead.)
 __device__ __forceinline__ bf16x8 load8(const uint16_t* p, bool ok) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     return __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const u32x4*>(p) : z);
@@ -164,34 +168,42 @@ __global__ __launch_bounds__(256) void linear_tiled_kernel(const LinearParams p)
     // read one 128-byte row segment.
     u32x4 ra[DEPTH][A_LD], rb[DEPTH][B_LD];
     const int nkb = (p.K + kTileK - 1) / kTileK;
+    // Addresses are clamped into the matrices, so every load is valid and
+    // unconditional (a branch around each load would make the compiler wait
+    // for all outstanding loads at the loop head, serialising the prefetch):
+    // rows past M of X and past N of W only feed outputs that are never
+    // stored, and blocks past the end are never copied to LDS. Only K elements
+    // past K (a K that is not a multiple of 64) are zeroed, at the LDS store of
+    // the last block.
     auto gload = [&](u32x4 (&a)[A_LD], u32x4 (&b)[B_LD], int kb) {
 #pragma unroll
         for (int q = 0; q < A_LD; ++q) {
             const int piece = q * 256 + tid, row = piece >> 3, k = kb * kTileK + 8 * (piece & 7);
-            const int m = m0 + row;
-            const bool ok = kb < nkb && m < p.M && k + 8 <= p.K;
-            a[q] = ok ? *reinterpret_cast<const u32x4*>(p.X + (int64_t)m * p.x_pitch + k)
-                      : u32x4{0u, 0u, 0u, 0u};
+            a[q] = *reinterpret_cast<const u32x4*>(
+                p.X + (int64_t)min(m0 + row, p.M - 1) * p.x_pitch + min(k, p.K - 8));
         }
 #pragma unroll
         for (int q = 0; q < B_LD; ++q) {
             const int piece = q * 256 + tid, row = piece >> 3, k = kb * kTileK + 8 * (piece & 7);
-            const int n = n0 + row;
-            const bool ok = kb < nkb && n < p.N && k + 8 <= p.K;
-            b[q] = ok ? *reinterpret_cast<const u32x4*>(p.W + (int64_t)n * p.K + k)
-                      : u32x4{0u, 0u, 0u, 0u};
+            b[q] = *reinterpret_cast<const u32x4*>(
+                p.W + (int64_t)min(n0 + row, p.N - 1) * p.K + min(k, p.K - 8));
         }
     };
-    auto lstore = [&](const u32x4 (&a)[A_LD], const u32x4 (&b)[B_LD], int buf) {
+    auto lstore = [&](const u32x4 (&a)[A_LD], const u32x4 (&b)[B_LD], int buf, int kb) {
+        const bool tail = kb * kTileK + kTileK > p.K;   // uniform
 #pragma unroll
         for (int q = 0; q < A_LD; ++q) {
             const int piece = q * 256 + tid;
-            *reinterpret_cast<u32x4*>(&sA[buf][piece >> 3][8 * (piece & 7)]) = a[q];
+            const bool ok = !tail || kb * kTileK + 8 * (piece & 7) + 8 <= p.K;
+            *reinterpret_cast<u32x4*>(&sA[buf][piece >> 3][8 * (piece & 7)]) =
+                ok ? a[q] : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int q = 0; q < B_LD; ++q) {
             const int piece = q * 256 + tid;
-            *reinterpret_cast<u32x4*>(&sB[buf][piece >> 3][8 * (piece & 7)]) = b[q];
+            const bool ok = !tail || kb * kTileK + 8 * (piece & 7) + 8 <= p.K;
+            *reinterpret_cast<u32x4*>(&sB[buf][piece >> 3][8 * (piece & 7)]) =
+                ok ? b[q] : u32x4{0u, 0u, 0u, 0u};
         }
     };
 
@@ -203,7 +215,7 @@ __global__ __launch_bounds__(256) void linear_tiled_kernel(const LinearParams p)
 
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) gload(ra[d], rb[d], d);
-    lstore(ra[0], rb[0], 0);
+    lstore(ra[0], rb[0], 0, 0);
     __syncthreads();
     for (int base = 0; base < nkb; base += DEPTH) {
 #pragma unroll
@@ -230,7 +242,7 @@ __global__ __launch_bounds__(256) void linear_tiled_kernel(const LinearParams p)
                     for (int j = 0; j < TN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
             }
-            if (kb + 1 < nkb) lstore(ra[(u + 1) % DEPTH], rb[(u + 1) % DEPTH], buf ^ 1);
+            if (kb + 1 < nkb) lstore(ra[(u + 1) % DEPTH], rb[(u + 1) % DEPTH], buf ^ 1, kb + 1);
             __syncthreads();
         }
     }
@@ -268,11 +280,12 @@ hipError_t launch_tiled(const LinearParams& p, hipStream_t s) {
 hipError_t launch_linear(const LinearParams& p, hipStream_t s) {
     // shapes measured on MI355X at the projections' sizes (7168 -> 6284,
     // 1536 -> 7168): 2 column tiles a wave and 8 waves for up to 64 rows,
-    // 128 x 64 LDS tiles above
+    // 128 x 64 LDS tiles with one K block in flight above (deeper register
+    // staging measured no faster)
     if (p.M <= 16) return launch_skinny<1, 2, 8>(p, s);
     if (p.M <= 32) return launch_skinny<2, 2, 8>(p, s);
     if (p.M <= 64) return launch_skinny<4, 2, 8>(p, s);
-    return launch_tiled<128, 64, 1>(p, s);
+    return launch_tiled<128, 64, 2>(p, s);
 }
 
 }  // namespace kda
