@@ -152,7 +152,10 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
     } else {
 #pragma unroll
         for (int t = 0; t < L; ++t) xb[t] = prow[t * p.pitch + 3 * (int64_t)D + (int64_t)h * N + cj];
-        if (cj < L) braw = prow[cj * p.pitch + 4 * (int64_t)D + kFaRank + h];
+        // unconditional (clamped row): a load under a per-lane branch here makes
+        // the compiler wait for every outstanding load before these waves issue
+        // their state stream
+        braw = prow[min(cj, L - 1) * p.pitch + 4 * (int64_t)D + kFaRank + h];
     }
 
     // ---- gate MFMA operands: wave w computes outputs 16w .. 16w + 15 of the head

@@ -194,3 +194,36 @@ def test_host_validation_leaves_device_untouched():
         assert g.core.device_errors() == 0
     finally:
         g.close()
+
+
+def test_padded_state_slot_stride_and_more_heads():
+    """A state pool whose slots carry padding (slot stride > H*128*128) and a head
+    count outside the workload set (H = 16, D = 2048)."""
+    import kimi_delta_attention_conv_amd as kda
+    from gpu_cases import OUT_SENTINEL
+    case = make_case(R=3, L=2, H=16, num_slots=9, seed=409, verify=True)
+    pad = 4096
+    unit = case.H * 128 * 128
+    before = case.state.numpy().copy()
+    ref = run_oracle(case)
+    big = torch.full((case.num_slots, unit + pad), -7.0, dtype=torch.float32)
+    big[:, :unit] = case.state.reshape(case.num_slots, unit)
+    dev = big.cuda()
+    state_view = torch.as_strided(dev, (case.num_slots, case.H, 128, 128),
+                                  (unit + pad, 128 * 128, 128, 1))
+    conv = case.conv_storage.cuda()
+    core = kda.KdaCore(conv_weight=case.conv_weight.cuda(), conv_bias=case.conv_bias.cuda(),
+                       f_b=case.f_b.cuda(), A_log=case.A_log.cuda(), dt_bias=case.dt_bias.cuda(),
+                       norm_weight=case.norm_weight.cuda(), gate_lower_bound=case.gate_lower_bound,
+                       norm_eps=case.norm_eps, l2_eps=case.l2_eps, conv=conv, state=state_view)
+    out = torch.full((case.S, case.D), OUT_SENTINEL, dtype=torch.int16).view(torch.bfloat16).cuda()
+    core.verify(case.projected.cuda(), out, case.slots.cuda(), case.accepted.cuda())
+    torch.cuda.synchronize()
+    host = dev.cpu()
+    assert torch.all(host[:, unit:] == -7.0), "slot padding was written"
+    got = dict(out=out.cpu().view(torch.int16).numpy().view(np.uint16),
+               conv=conv.cpu().view(torch.int16).numpy().view(np.uint16),
+               state=host[:, :unit].reshape(case.num_slots, case.H, 128, 128).numpy(),
+               errors=core.device_errors())
+    core.close()
+    assert_parity(case, ref, got, before, label="padded slot stride, H=16")
