@@ -88,6 +88,11 @@ kda::CoreParams core_params(const kda_handle_s* h, const void* projected, int64_
     p.q_scale = 1.0f / std::sqrt((float)kda::kHeadDim);
     p.norm_eps = h->norm_eps;
     p.l2_eps = h->l2_eps;
+    // the dim-first pool [slots][3D][3] with 16-byte aligned slots takes the
+    // kernel's coalesced window stores (each head's q, k, v windows are three
+    // contiguous 768-byte runs whose starts are multiples of 16 bytes)
+    p.conv_dim_first16 = h->caches.conv_pos_stride == 1 && h->caches.conv_dim_stride == 3 &&
+                         h->caches.conv_slot_stride % 8 == 0 && aligned(h->caches.conv, 16);
     return p;
 }
 

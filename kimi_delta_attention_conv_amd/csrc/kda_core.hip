@@ -104,6 +104,10 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
     __shared__ float s_braw[L];
     __shared__ float s_beta[L];
     __shared__ float s_kq[L];           // k_hat . q_hat
+    // conv windows after each token in the dim-first layout: channel cl's three
+    // inputs at 3 cl .. 3 cl + 2 (the global order of one head's q, k, v runs)
+    __shared__ __attribute__((aligned(16))) uint16_t s_win[L][3 * N * 3];
+    __shared__ int s_dst[L];
 
     // ---- slot resolution ([prepared] run: slots [B], or [>= B, q] + accepted)
     const int32_t* srow = p.slots + (int64_t)r * p.slots_row_stride;
@@ -124,6 +128,7 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
         if (h == 0 && tid == 0) atomicAdd(p.err_count, 1);
         return;
     }
+    if (tid < L) s_dst[tid] = srow[tid];
 
     const int64_t row0 = (int64_t)r * L;
     const uint16_t* prow = p.projected + row0 * p.pitch;
@@ -223,10 +228,16 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
             s_qkv[t][cl] = pre * sigmoid(pre);
             w0 = w1; w1 = w2; w2 = x;
             b0 = b1; b1 = b2; b2 = xb[t];
-            uint16_t* cw_out = p.conv + (int64_t)dst[t] * p.conv_slot_stride + cch * p.conv_dim_stride;
-            cw_out[0] = (uint16_t)b0;
-            cw_out[p.conv_pos_stride] = (uint16_t)b1;
-            cw_out[2 * p.conv_pos_stride] = (uint16_t)b2;
+            if (p.conv_dim_first16) {   // staged; written below with 16-byte stores
+                s_win[t][3 * cl] = (uint16_t)b0;
+                s_win[t][3 * cl + 1] = (uint16_t)b1;
+                s_win[t][3 * cl + 2] = (uint16_t)b2;
+            } else {
+                uint16_t* cw_out = p.conv + (int64_t)dst[t] * p.conv_slot_stride + cch * p.conv_dim_stride;
+                cw_out[0] = (uint16_t)b0;
+                cw_out[p.conv_pos_stride] = (uint16_t)b1;
+                cw_out[2 * p.conv_pos_stride] = (uint16_t)b2;
+            }
         }
     } else {
 #pragma unroll
@@ -324,6 +335,22 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
         const uint32_t packed = f32_to_bf16(y0) | (f32_to_bf16(y1) << 16);
         uint32_t* op = reinterpret_cast<uint32_t*>(p.out + (row0 + t) * D + (int64_t)h * N + 2 * lane);
         *op = packed;
+    }
+
+    // ---- coalesced conv window stores (dim-first pool): per token, the head's
+    // q, k and v windows are 3 runs of 128 channels x 3 bf16 = 768 B, i.e.
+    // 48 chunks of 16 B each; 2-byte stores at a 6-byte stride cost far more
+    // than their bytes. Issued last, after the state stores and core_out, so they
+    // do not queue ahead of the state traffic that bounds the kernel; s_win and
+    // s_dst are filled before the first barrier and never overwritten.
+    if (p.conv_dim_first16) {
+        constexpr int kChunks = 3 * 48;
+        for (int c = tid; c < L * kChunks; c += kThreads) {
+            const int t = c / kChunks, k = c - t * kChunks, s = k / 48;
+            uint16_t* out = p.conv + (int64_t)s_dst[t] * p.conv_slot_stride +
+                            ((int64_t)s * D + (int64_t)h * N) * 3 + (k - s * 48) * 8;
+            *reinterpret_cast<u32x4*>(out) = *reinterpret_cast<const u32x4*>(&s_win[t][8 * k]);
+        }
     }
 }
 

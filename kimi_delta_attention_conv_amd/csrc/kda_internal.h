@@ -49,6 +49,7 @@ struct CoreParams {
     float q_scale;
     float norm_eps;
     float l2_eps;
+    int32_t conv_dim_first16;   // conv pool is dim first [slots][3D][3], 16-byte aligned
 };
 
 // Raw inputs of the weight re-layout kernel (device pointers).

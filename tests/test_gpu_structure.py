@@ -227,3 +227,31 @@ def test_padded_state_slot_stride_and_more_heads():
                errors=core.device_errors())
     core.close()
     assert_parity(case, ref, got, before, label="padded slot stride, H=16")
+
+
+def test_conv_fast_and_generic_store_paths_agree():
+    """A dim-first conv pool with a 16-byte aligned base takes the staged 16-byte
+    window stores; the same pool one element off alignment takes the per-element
+    path. Both must give bit-identical pools, states and outputs."""
+    import kimi_delta_attention_conv_amd as kda
+    case = make_case(R=5, L=4, H=3, num_slots=24, seed=410, verify=True)
+    results = []
+    for offset in (0, 1):
+        flat = torch.zeros(case.conv_storage.numel() + 8, dtype=torch.bfloat16)
+        flat[offset: offset + case.conv_storage.numel()] = case.conv_storage.reshape(-1)
+        dflat = flat.cuda()
+        conv = torch.as_strided(dflat, case.conv_storage.shape, case.conv_storage.stride(), offset)
+        state = case.state.cuda()
+        core = kda.KdaCore(conv_weight=case.conv_weight.cuda(), conv_bias=case.conv_bias.cuda(),
+                           f_b=case.f_b.cuda(), A_log=case.A_log.cuda(),
+                           dt_bias=case.dt_bias.cuda(), norm_weight=case.norm_weight.cuda(),
+                           gate_lower_bound=case.gate_lower_bound, norm_eps=case.norm_eps,
+                           l2_eps=case.l2_eps, conv=conv, state=state)
+        out = torch.zeros(case.S, case.D, dtype=torch.bfloat16, device="cuda")
+        core.verify(case.projected.cuda(), out, case.slots.cuda(), case.accepted.cuda())
+        torch.cuda.synchronize()
+        assert core.device_errors() == 0
+        core.close()
+        results.append((conv.cpu().view(torch.int16), state.cpu(), out.cpu().view(torch.int16)))
+    for a, b in zip(results[0], results[1]):
+        assert torch.equal(a, b)
