@@ -28,6 +28,10 @@ seed (fp32 draws; bf16 by round-to-nearest-even cast):
  12. beta_raw columns [S, H]         ~ N(0, beta_std^2), written over the
                                        projected beta columns (only when
                                        beta_std != 1)
+
+With `pool_device` set (pools of many gigabytes), steps 4 and 5 are drawn instead
+on that device, from a generator of that device seeded with the case's seed
+(conv pool first, then state pool), and the CPU generator goes on at step 6.
 """
 from __future__ import annotations
 
@@ -110,7 +114,8 @@ def make_case(R: int, L: int, H: int, num_slots: int, seed: int, *, name: str = 
               verify: Optional[bool] = None, pitch: Optional[int] = None,
               conv_dim_first: bool = True, with_bias: bool = True, beta_std: float = 1.0,
               a_log_range=(-1.0, 1.0), fixed_slot: Optional[int] = None,
-              block_table_cols: Optional[int] = None, W: int = CONV_WIDTH) -> Case:
+              block_table_cols: Optional[int] = None, W: int = CONV_WIDTH,
+              pool_device: Optional[str] = None) -> Case:
     if verify is None:
         verify = L > 1
     if not verify and L != 1:
@@ -131,11 +136,15 @@ def make_case(R: int, L: int, H: int, num_slots: int, seed: int, *, name: str = 
     conv_weight = (randn(C, W) * 0.5).to(torch.bfloat16).view(C, 1, W)
     bias_draw = (randn(C) * 0.1).to(torch.bfloat16)
     conv_bias = bias_draw if with_bias else None
-    if conv_dim_first:
-        conv_storage = randn(num_slots, C, W - 1).to(torch.bfloat16)
+    conv_shape = (num_slots, C, W - 1) if conv_dim_first else (num_slots, W - 1, C)
+    if pool_device is None:
+        conv_storage = randn(*conv_shape).to(torch.bfloat16)
+        state = randn(num_slots, H, HEAD_DIM, HEAD_DIM) * 0.05
     else:
-        conv_storage = randn(num_slots, W - 1, C).to(torch.bfloat16)
-    state = randn(num_slots, H, HEAD_DIM, HEAD_DIM) * 0.05
+        dgen = torch.Generator(device=pool_device).manual_seed(seed)
+        conv_storage = torch.randn(conv_shape, generator=dgen, device=pool_device).to(torch.bfloat16)
+        state = torch.randn((num_slots, H, HEAD_DIM, HEAD_DIM), generator=dgen,
+                            device=pool_device).mul_(0.05)
     f_b = (randn(D, FA_RANK) * 0.09).to(torch.bfloat16)
     lo, hi = a_log_range
     A_log = rand(H) * (hi - lo) + lo
