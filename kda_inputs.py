@@ -29,6 +29,11 @@ seed (fp32 draws; bf16 by round-to-nearest-even cast):
                                        projected beta columns (only when
                                        beta_std != 1)
 
+ 13. coarse gate operands (only with coarse_gate): f_b [D, 128] = k 2^-8 and the
+     projected f_a columns [S, 128] = k 2^-4, k ~ U{-31 .. 31} (f_b first). Every
+     product is a multiple of 2^-12 and a sum of 128 of them stays below 2^12, so
+     g1 = f_b f_a is exact in fp32 in any summation order.
+
 With `pool_device` set (pools of many gigabytes), steps 4 and 5 are drawn instead
 on that device, from a generator of that device seeded with the case's seed
 (conv pool first, then state pool), and the CPU generator goes on at step 6.
@@ -115,7 +120,7 @@ def make_case(R: int, L: int, H: int, num_slots: int, seed: int, *, name: str = 
               conv_dim_first: bool = True, with_bias: bool = True, beta_std: float = 1.0,
               a_log_range=(-1.0, 1.0), fixed_slot: Optional[int] = None,
               block_table_cols: Optional[int] = None, W: int = CONV_WIDTH,
-              pool_device: Optional[str] = None) -> Case:
+              pool_device: Optional[str] = None, coarse_gate: bool = False) -> Case:
     if verify is None:
         verify = L > 1
     if not verify and L != 1:
@@ -170,6 +175,10 @@ def make_case(R: int, L: int, H: int, num_slots: int, seed: int, *, name: str = 
     if beta_std != 1.0:
         beta = (randn(S, H) * beta_std).to(torch.bfloat16)
         projected[:, 4 * D + FA_RANK: 4 * D + FA_RANK + H] = beta
+    if coarse_gate:
+        f_b = (torch.randint(-31, 32, (D, FA_RANK), generator=gen).float() * 2.0 ** -8).to(torch.bfloat16)
+        f_a = (torch.randint(-31, 32, (S, FA_RANK), generator=gen).float() * 2.0 ** -4).to(torch.bfloat16)
+        projected[:, 4 * D: 4 * D + FA_RANK] = f_a
 
     return Case(name=name, seed=seed, R=R, L=L, H=H, W=W, num_slots=num_slots, pitch=pitch,
                 verify=verify, projected=projected, conv_weight=conv_weight,

@@ -39,6 +39,9 @@ class Problem(ctypes.Structure):
         ("gate_lower_bound", ctypes.c_double), ("q_scale", ctypes.c_double),
         ("norm_eps", ctypes.c_double), ("l2_eps", ctypes.c_double),
         ("core_out", ctypes.c_void_p), ("core_out_f64", ctypes.c_void_p),
+        ("handoff_bf16", ctypes.c_int32), ("ties", ctypes.c_void_p),
+        ("tie_conv", ctypes.c_double), ("tie_g1", ctypes.c_double),
+        ("tie_o", ctypes.c_double), ("tie_y", ctypes.c_double),
     ]
 
 
@@ -78,7 +81,7 @@ class Oracle:
         lib.kda_ref_double_to_bf16.restype = ctypes.c_uint16
         lib.kda_ref_conv_token.argtypes = [i32, i32, p, p, p, p, p]
         lib.kda_ref_conv_token.restype = None
-        lib.kda_ref_gate.argtypes = [i32, p, p, p, p, d, p]
+        lib.kda_ref_gate.argtypes = [i32, p, p, p, p, d, i32, p]
         lib.kda_ref_gate.restype = None
         lib.kda_ref_l2norm.argtypes = [i32, p, d, d, p]
         lib.kda_ref_l2norm.restype = None
@@ -122,14 +125,15 @@ class Oracle:
         self.lib.kda_ref_conv_token(C, W, _ptr(w), _ptr(b), _ptr(win), _ptr(x), _ptr(y))
         return y, win
 
-    def gate(self, f_b, f_a, A_log, dt_bias, lb):
-        """Decay gate g [D] of one token; f_b [D][128], f_a [128], A_log [H], dt_bias [D]."""
+    def gate(self, f_b, f_a, A_log, dt_bias, lb, round_g1=False):
+        """Decay gate g [D] of one token; f_b [D][128], f_a [128], A_log [H], dt_bias [D].
+        With round_g1, g1 = f_b f_a is rounded to bf16 first (the hand-off mode)."""
         f_b, f_a, A_log, dt_bias = _f64(f_b), _f64(f_a), _f64(A_log), _f64(dt_bias)
         H = A_log.size
         assert f_b.shape == (H * HEAD_DIM, FA_RANK) and f_a.size == FA_RANK
         g = np.zeros(H * HEAD_DIM)
         self.lib.kda_ref_gate(H, _ptr(f_b), _ptr(f_a), _ptr(A_log), _ptr(dt_bias), float(lb),
-                              _ptr(g))
+                              int(bool(round_g1)), _ptr(g))
         return g
 
     def l2norm(self, x, eps, scale=1.0):
@@ -185,12 +189,18 @@ class Oracle:
     def run(self, *, heads, width, requests, tokens, projected, pitch, slots, slots_row_stride,
             accepted, num_slots, conv, conv_strides, state, state_slot_stride, conv_weight,
             conv_bias, f_b, A_log, dt_bias, norm_weight, norm_head_stride, gate_lower_bound,
-            norm_eps, l2_eps, core_out, q_scale=HEAD_DIM ** -0.5, core_out_f64=None) -> int:
+            norm_eps, l2_eps, core_out, q_scale=HEAD_DIM ** -0.5, core_out_f64=None,
+            handoff_bf16=False, ties=None, tie_margins=(0.0, 0.0, 0.0, 0.0)) -> int:
         """One decode (accepted=None) or verify call, in place on host arrays.
 
         bf16 arrays are uint16 bit patterns. `conv`, `state` (whole pools) and
         `core_out` must be C-contiguous numpy arrays; they are updated in
-        place. Returns the number of skipped requests."""
+        place. Returns the number of skipped requests.
+
+        handoff_bf16 rounds conv out, g1 and o to bf16 where produced. `ties`,
+        an int32 array [R, H, 4] zeroed by the caller, receives per (request,
+        head) the near-tie counts of conv out, g1, o and core_out under the
+        relative margins `tie_margins` (conv, g1, o, core_out)."""
         projected = _u16(projected)
         slots = np.ascontiguousarray(np.asarray(slots, dtype=np.int32))
         acc = None if accepted is None else np.ascontiguousarray(
@@ -207,6 +217,9 @@ class Oracle:
         norm_weight = np.ascontiguousarray(np.asarray(norm_weight, dtype=np.float32))
         if core_out_f64 is not None:
             assert core_out_f64.dtype == np.float64 and core_out_f64.flags.c_contiguous
+        if ties is not None:
+            assert ties.dtype == np.int32 and ties.flags.c_contiguous
+            assert ties.size == requests * heads * 4
         pr = Problem(
             heads=heads, width=width, requests=requests, tokens=tokens,
             projected=_ptr(projected), pitch=pitch, slots=_ptr(slots),
@@ -218,7 +231,9 @@ class Oracle:
             dt_bias=_ptr(dt_bias), norm_weight=_ptr(norm_weight),
             norm_head_stride=norm_head_stride, gate_lower_bound=gate_lower_bound,
             q_scale=q_scale, norm_eps=norm_eps, l2_eps=l2_eps, core_out=_ptr(core_out),
-            core_out_f64=_ptr(core_out_f64))
+            core_out_f64=_ptr(core_out_f64), handoff_bf16=int(bool(handoff_bf16)),
+            ties=_ptr(ties), tie_conv=float(tie_margins[0]), tie_g1=float(tie_margins[1]),
+            tie_o=float(tie_margins[2]), tie_y=float(tie_margins[3]))
         rc = self.lib.kda_ref_run(ctypes.byref(pr))
         if rc < 0:
             raise ValueError("oracle rejected the problem description")

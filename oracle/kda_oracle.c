@@ -18,16 +18,36 @@
  * print no formula; the formulas below are the plain readings of those steps.
  *
  * Arithmetic: every step is evaluated in IEEE double, in the order written.
- * Values are rounded only where they are stored: the recurrent state to fp32
+ * Values are rounded where they are stored: the recurrent state to fp32
  * (round-to-nearest-even) after every token, core_out to bf16 (RNE), conv
  * windows copied exactly (they hold bf16 inputs). Carrying the fp32-rounded
  * state makes a verify call over L tokens equal L chained decode calls bit
  * for bit.
  *
+ * Two rounding modes. Fused (handoff_bf16 = 0): nothing else is rounded.
+ * Hand-off (handoff_bf16 = 1): the values an unfused pipeline passes between
+ * its kernels as bf16 are rounded to bf16 (RNE) where they are produced --
+ * the conv + SiLU outputs q|k|v, g1 = f_b f_a, and the recurrence output o --
+ * which is the [kda] page's rounding rule (module docstring: elementwise
+ * rounding follows the original path at every bf16 hand-off between the
+ * original kernels).
+ *
+ * Near-tie counters (hand-off checks). Another implementation computes each
+ * rounded value in its own precision, so its rounding can differ from this
+ * one's where the value lies close to a bf16 rounding boundary. Given a
+ * caller's margin m for a value x (a bound on that implementation's error in
+ * x), x counts as a near tie when x - m and x + m round to different bf16
+ * values. Margins are relative factors times a magnitude: for a conv output
+ * |bias| + sum |w * input|; for g1 sum |f_b f_a| (zero when every term is a
+ * multiple of one quantum Q and the sum of |terms| is at most 2^24 Q, where
+ * any fp32 summation order is exact); for o the sum over i of |S_dec q_i|
+ * plus |beta| (|v| + sum |S_dec k_i|) sum |k_i q_i| (S_dec: the decayed
+ * state row); for the core_out value its own magnitude.
+ *
  * Parity status: every step has a pin in the CPU tests (closed forms,
  * invariants, library routines, brute force). Readings that no printed value
- * fixes -- the l2norm epsilon, the norm-weight shape, no bf16 rounding
- * between fused steps -- are the adopted readings, not pinned by the pages.
+ * fixes -- the l2norm epsilon, the norm-weight shape -- are the adopted
+ * readings, not pinned by the pages.
  */
 #include <math.h>
 #include <stdint.h>
@@ -115,15 +135,17 @@ void kda_ref_conv_token(int32_t C, int32_t W, const double* w, const double* bia
  *   g1[i] = sum_m f_b[i][m] * f_a[m]               (f_b is [D][128])
  *   g[i]  = lb * sigmoid(exp(A_log[i / 128]) * (g1[i] + dt_bias[i]))
  * A_log has one value per head ([prepared] PreparedKda.__init__: heads =
- * A_log.numel()); dt_bias has one per channel. */
+ * A_log.numel()); dt_bias has one per channel. With round_g1, g1 is rounded
+ * to bf16 before the gate (the hand-off mode). */
 void kda_ref_gate(int32_t H, const double* f_b, const double* f_a, const double* A_log,
-                  const double* dt_bias, double lb, double* g)
+                  const double* dt_bias, double lb, int32_t round_g1, double* g)
 {
     const int32_t D = H * KDA_REF_HEAD_DIM;
     for (int32_t i = 0; i < D; ++i) {
         double g1 = 0.0;
         for (int32_t m = 0; m < KDA_REF_FA_RANK; ++m)
             g1 += f_b[(int64_t)i * KDA_REF_FA_RANK + m] * f_a[m];
+        if (round_g1) g1 = kda_ref_bf16_to_double(kda_ref_double_to_bf16(g1));   /* hand-off */
         double a = exp(A_log[i / KDA_REF_HEAD_DIM]);
         g[i] = lb * kda_ref_sigmoid(a * (g1 + dt_bias[i]));
     }
@@ -213,7 +235,43 @@ typedef struct {
     double l2_eps;
     uint16_t* core_out;         /* bf16 [S][D] */
     double* core_out_f64;       /* optional [S][D]: the value before the bf16 rounding */
+    int32_t handoff_bf16;       /* 0 fused; 1 bf16 hand-offs (conv out, g1, o) */
+    int32_t* ties;              /* optional [R][H][4]: near ties of conv out, g1, o, core_out */
+    double tie_conv, tie_g1, tie_o, tie_y;   /* relative margins (see the header) */
 } kda_ref_problem;
+
+/* bf16 rounding of x could go either way within +-m. */
+static int near_tie(double x, double m)
+{
+    return m > 0.0 && kda_ref_double_to_bf16(x - m) != kda_ref_double_to_bf16(x + m);
+}
+
+/* The lowest set bit of a nonzero double: |a| = M 2^k with M odd gives 2^k. */
+static double lowest_bit(double a)
+{
+    int e;
+    double m = frexp(fabs(a), &e);      /* |a| = m 2^e, m in [0.5, 1) */
+    int64_t M = (int64_t)ldexp(m, 53);  /* exact: 53 significant bits */
+    int k = e - 53;
+    while ((M & 1) == 0) { M >>= 1; ++k; }
+    return ldexp(1.0, k);
+}
+
+/* Margin of g1 = sum_m f_b[m] f_a[m] for an fp32 implementation: zero when
+ * the sum is exact in fp32 in any order, else rel * sum |terms|. */
+static double g1_margin(const double* fbrow, const double* fa, double rel)
+{
+    double mag = 0.0, q = INFINITY;
+    for (int32_t m = 0; m < KDA_REF_FA_RANK; ++m) {
+        const double t = fbrow[m] * fa[m];
+        if (t == 0.0) continue;
+        mag += fabs(t);
+        const double qt = lowest_bit(fbrow[m]) * lowest_bit(fa[m]);
+        if (qt < q) q = qt;
+    }
+    if (mag == 0.0 || mag <= ldexp(q, 24)) return 0.0;
+    return rel * mag;
+}
 
 /* Slot resolution ([prepared] PreparedKda.run and _operands: slots [B] for a
  * decode step; slots [>= B, q] with accepted [>= B] for a verify step).
@@ -267,7 +325,10 @@ int32_t kda_ref_run(const kda_ref_problem* p)
     double* o = malloc(sizeof(double) * (size_t)N);
     double* gate = malloc(sizeof(double) * (size_t)N);
     double* yo = malloc(sizeof(double) * (size_t)N);
+    double* cmag = malloc(sizeof(double) * (size_t)C);
+    double* omag = malloc(sizeof(double) * (size_t)N);
     int32_t* dst = malloc(sizeof(int32_t) * (size_t)L);
+    const int hand = p->handoff_bf16 != 0;
     for (int64_t i = 0; i < (int64_t)C * W; ++i) w[i] = kda_ref_bf16_to_double(p->conv_weight[i]);
     if (b)
         for (int32_t c = 0; c < C; ++c) b[c] = kda_ref_bf16_to_double(p->conv_bias[c]);
@@ -297,14 +358,36 @@ int32_t kda_ref_run(const kda_ref_problem* p)
             for (int64_t e = 0; e < p->pitch; ++e) x[e] = kda_ref_bf16_to_double(xr[e]);
 
             /* conv update + SiLU over q|k|v; the new window goes to dst[t] */
+            if (p->ties && hand)
+                for (int32_t c = 0; c < C; ++c) {
+                    double mg = b ? fabs(b[c]) : 0.0;
+                    for (int32_t m = 0; m < W - 1; ++m)
+                        mg += fabs(w[(int64_t)c * W + m] * win[(int64_t)c * (W - 1) + m]);
+                    cmag[c] = mg + fabs(w[(int64_t)c * W + W - 1] * x[c]);
+                }
             kda_ref_conv_token(C, W, w, b, win, x, y);
+            if (hand)
+                for (int32_t c = 0; c < C; ++c) {
+                    if (p->ties && near_tie(y[c], p->tie_conv * cmag[c]))
+                        ++p->ties[((int64_t)r * H + (c % D) / N) * 4 + 0];
+                    y[c] = kda_ref_bf16_to_double(kda_ref_double_to_bf16(y[c]));   /* hand-off */
+                }
             for (int32_t c = 0; c < C; ++c)
                 for (int32_t m = 0; m < W - 1; ++m)
                     p->conv[dst[t] * p->conv_slot_stride + c * p->conv_dim_stride + m * p->conv_pos_stride] =
                         kda_ref_double_to_bf16(win[(int64_t)c * (W - 1) + m]);
 
             /* decay gate from f_a = projected[4D : 4D + 128] */
-            kda_ref_gate(H, fb, x + 4 * (int64_t)D, alog, dtb, p->gate_lower_bound, g);
+            kda_ref_gate(H, fb, x + 4 * (int64_t)D, alog, dtb, p->gate_lower_bound, hand, g);
+            if (p->ties && hand)
+                for (int32_t i = 0; i < D; ++i) {
+                    const double* fbrow = fb + (int64_t)i * KDA_REF_FA_RANK;
+                    const double* fa = x + 4 * (int64_t)D;
+                    double g1 = 0.0;
+                    for (int32_t m = 0; m < KDA_REF_FA_RANK; ++m) g1 += fbrow[m] * fa[m];
+                    if (near_tie(g1, g1_margin(fbrow, fa, p->tie_g1)))
+                        ++p->ties[((int64_t)r * H + i / N) * 4 + 1];
+                }
 
             for (int32_t h = 0; h < H; ++h) {
                 /* beta = sigmoid(projected[4D + 128 + h]), one per (token, head) */
@@ -313,7 +396,27 @@ int32_t kda_ref_run(const kda_ref_problem* p)
                 kda_ref_l2norm(N, y + D + (int64_t)h * N, p->l2_eps, 1.0, kh);
                 const double* v = y + 2 * (int64_t)D + (int64_t)h * N;
                 double* Sh = S + (int64_t)h * N * N;
+                if (p->ties && hand) {
+                    const double* gh = g + (int64_t)h * N;
+                    double kq = 0.0;
+                    for (int32_t i = 0; i < N; ++i) kq += fabs(kh[i] * qh[i]);
+                    for (int32_t j = 0; j < N; ++j) {
+                        double aq = 0.0, ak = 0.0;
+                        for (int32_t i = 0; i < N; ++i) {
+                            const double sd = Sh[(int64_t)j * N + i] * exp(gh[i]);
+                            aq += fabs(sd * qh[i]);
+                            ak += fabs(sd * kh[i]);
+                        }
+                        omag[j] = aq + fabs(beta) * (fabs(v[j]) + ak) * kq;
+                    }
+                }
                 kda_ref_recur_token(N, N, Sh, g + (int64_t)h * N, kh, qh, v, beta, o);
+                if (hand)
+                    for (int32_t j = 0; j < N; ++j) {
+                        if (p->ties && near_tie(o[j], p->tie_o * omag[j]))
+                            ++p->ties[((int64_t)r * H + h) * 4 + 2];
+                        o[j] = kda_ref_bf16_to_double(kda_ref_double_to_bf16(o[j]));   /* hand-off */
+                    }
 
                 /* the state written for this token, rounded to fp32 and carried */
                 float* out_state = p->state + dst[t] * p->state_slot_stride + (int64_t)h * N * N;
@@ -330,13 +433,16 @@ int32_t kda_ref_run(const kda_ref_problem* p)
                     int64_t oi = row * D + (int64_t)h * N + j;
                     p->core_out[oi] = kda_ref_double_to_bf16(yo[j]);
                     if (p->core_out_f64) p->core_out_f64[oi] = yo[j];
+                    if (p->ties && near_tie(yo[j], p->tie_y * fabs(yo[j])))
+                        ++p->ties[((int64_t)r * H + h) * 4 + 3];
                 }
             }
         }
     }
 
     free(w); free(b); free(fb); free(alog); free(dtb); free(nw); free(win); free(S); free(x);
-    free(y); free(g); free(qh); free(kh); free(o); free(gate); free(yo); free(dst);
+    free(y); free(g); free(qh); free(kh); free(o); free(gate); free(yo); free(cmag); free(omag);
+    free(dst);
     return skipped;
 }
 

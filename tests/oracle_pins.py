@@ -510,3 +510,122 @@ def check_linear_against_numpy_and_closed_forms(orc):
     assert np.array_equal(y_oh, w.T)
     ms, ns = rng.integers(0, M, 20), rng.integers(0, N, 20)
     _close(orc.linear_entries(x, w, ms, ns, x_pitch=pitch), y64[ms, ns], 0, 0, "entries")
+
+
+# ----------------------------------------------------------------- bf16 hand-off mode
+
+def _bf16_rne(x):
+    """Round float64 values to bf16 (8 significant bits, ties to even), in numpy."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(np.abs(x))
+    q = np.ldexp(1.0, np.maximum(e - 8, -133))
+    return np.copysign(np.round(np.abs(x) / q) * q, x)
+
+
+def _near_ties(x, m):
+    return int(np.count_nonzero(_bf16_rne(x - m) != _bf16_rne(x + m)))
+
+
+def _conv_outputs(case, conv_slot, x):
+    """SiLU(conv) of one token via torch conv1d, and |bias| + sum |w * input| per channel."""
+    D = case.D
+    conv0 = om.bf16_bits_to_f64(bf16_np(case.conv_view()))[conv_slot]
+    w = om.bf16_bits_to_f64(bf16_np(case.conv_weight))                   # [3D, 1, W]
+    b = om.bf16_bits_to_f64(bf16_np(case.conv_bias))
+    seq = np.concatenate([conv0, x[:3 * D, None]], 1)                   # [3D, W]
+    y = torch.nn.functional.silu(torch.nn.functional.conv1d(
+        torch.from_numpy(seq)[None], torch.from_numpy(w), torch.from_numpy(b),
+        groups=3 * D))[0, :, 0].numpy()
+    mag = np.abs(b) + np.abs(w[:, 0, :] * seq).sum(1)
+    return y, mag
+
+
+@pin
+def check_handoff_zero_state_closed_form(orc):
+    """Hand-off mode, zero carried state, one token: q, k, v are the bf16-rounded
+    SiLU(conv) outputs, the written state is beta v_r k_r^T (normalised k_r), o =
+    beta (k.q) v_r is rounded to bf16 before the gated RMSNorm; and the near-tie
+    counts of conv out, o and core_out equal brute-force counts over the same values."""
+    case = make_case(R=2, L=1, H=2, num_slots=4, seed=26, verify=False)
+    mu = 2.0 ** -10
+    ties = np.zeros((case.R, case.H, 4), np.int32)
+    res = run_oracle(case, orc, state=torch.zeros_like(case.state), handoff_bf16=True,
+                     ties=ties, tie_margins=(mu, 0.0, mu, mu))
+    D = case.D
+    for r in range(case.R):
+        slot = int(case.slots[r])
+        x = om.bf16_bits_to_f64(bf16_np(case.projected[r]))
+        y, mag = _conv_outputs(case, slot, x)
+        yr = _bf16_rne(y)
+        for h in range(case.H):
+            seg = [slice(s * D + 128 * h, s * D + 128 * (h + 1)) for s in range(3)]
+            conv_ties = sum(_near_ties(y[sl], mu * mag[sl]) for sl in seg)
+            q, k, v = (yr[sl] for sl in seg)
+            kh = k / np.sqrt(np.dot(k, k) + case.l2_eps)
+            qh = q / np.sqrt(np.dot(q, q) + case.l2_eps) * 128 ** -0.5
+            beta = scipy.special.expit(x[4 * D + 128 + h])
+            _close(res["state"][slot, h], np.float32(beta * np.outer(v, kh)), 2e-7, 1e-30,
+                   "hand-off state")
+            o = beta * np.dot(kh, qh) * v
+            o_ties = _near_ties(o, mu * abs(beta) * np.abs(v) * np.abs(kh * qh).sum())
+            orr = _bf16_rne(o)
+            gate = x[3 * D + 128 * h: 3 * D + 128 * (h + 1)]
+            exp = orr / np.sqrt(np.mean(orr * orr) + case.norm_eps) \
+                * case.norm_weight.numpy() * scipy.special.expit(gate)
+            _close(res["out_f64"][r, 128 * h: 128 * (h + 1)], exp, 1e-9, 1e-12, "hand-off core_out")
+            y_ties = _near_ties(exp, mu * np.abs(exp))
+            assert tuple(ties[r, h]) == (conv_ties, 0, o_ties, y_ties), (r, h, ties[r, h],
+                                                                          (conv_ties, o_ties, y_ties))
+    assert ties[:, :, 0].sum() > 0 and ties[:, :, 2].sum() > 0 and ties[:, :, 3].sum() > 0
+
+
+@pin
+def check_handoff_g1_rounding_closed_form(orc):
+    """Hand-off mode with beta = 0: the written state is the carried state decayed by
+    e^g per key column, g = lb sigmoid(e^A_log (bf16(f_b f_a) + dt_bias)), with g1
+    from numpy in float64 and rounded to bf16; the fused mode decays by the unrounded
+    g1 instead."""
+    case = make_case(R=2, L=1, H=2, num_slots=4, seed=31, verify=False)
+    D = case.D
+    proj = case.projected.clone()
+    proj[:, 4 * D + 128: 4 * D + 128 + case.H] = float("-inf")
+    f_b = om.bf16_bits_to_f64(bf16_np(case.f_b))
+    before = case.state.numpy().astype(np.float64)
+    for hand in (True, False):
+        res = run_oracle(case, orc, projected=proj, handoff_bf16=hand)
+        for r in range(case.R):
+            slot = int(case.slots[r])
+            f_a = om.bf16_bits_to_f64(bf16_np(proj[r, 4 * D: 4 * D + 128]))
+            g1 = f_b @ f_a
+            if hand:
+                g1 = _bf16_rne(g1)
+            a = np.repeat(np.exp(case.A_log.numpy().astype(np.float64)), 128)
+            g = case.gate_lower_bound * scipy.special.expit(a * (g1 + case.dt_bias.numpy()))
+            exp = before[slot] * np.exp(g).reshape(case.H, 1, 128)
+            _close(res["state"][slot], exp, 2e-7, 1e-30, f"decay, hand-off={hand}")
+
+
+@pin
+def check_handoff_g1_tie_certificate(orc):
+    """g1 near ties: with coarse gate operands every fp32 sum is exact, so no g1
+    value is a near tie even at a margin factor of 1 (while conv outputs are); with
+    ordinary operands the count equals a brute-force count at factor 2^-10."""
+    case = make_case(R=2, L=1, H=2, num_slots=4, seed=32, verify=False, coarse_gate=True)
+    ties = np.zeros((case.R, case.H, 4), np.int32)
+    run_oracle(case, orc, handoff_bf16=True, ties=ties, tie_margins=(1.0, 1.0, 0.0, 0.0))
+    assert ties[:, :, 1].sum() == 0 and ties[:, :, 0].sum() > 0, ties
+
+    case = make_case(R=2, L=1, H=2, num_slots=4, seed=33, verify=False)
+    mu = 2.0 ** -10
+    ties = np.zeros((case.R, case.H, 4), np.int32)
+    run_oracle(case, orc, handoff_bf16=True, ties=ties, tie_margins=(0.0, mu, 0.0, 0.0))
+    f_b = om.bf16_bits_to_f64(bf16_np(case.f_b))
+    D = case.D
+    for r in range(case.R):
+        f_a = om.bf16_bits_to_f64(bf16_np(case.projected[r, 4 * D: 4 * D + 128]))
+        g1 = f_b @ f_a
+        mag = np.abs(f_b * f_a[None, :]).sum(1)
+        for h in range(case.H):
+            sl = slice(128 * h, 128 * (h + 1))
+            assert ties[r, h, 1] == _near_ties(g1[sl], mu * mag[sl]), (r, h)
+    assert ties[:, :, 1].sum() > 0

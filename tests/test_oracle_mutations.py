@@ -52,6 +52,22 @@ MUTATIONS = {
                                  "const uint16_t* wr = w + (int64_t)n;\n            double acc"),
     "linear_ignores_pitch": ("for (int32_t k = 0; k < K; ++k) xr[k] = kda_ref_bf16_to_double(x[(int64_t)m * x_pitch + k]);",
                              "for (int32_t k = 0; k < K; ++k) xr[k] = kda_ref_bf16_to_double(x[(int64_t)m * K + k]);"),
+    "handoff_conv_not_rounded": (
+        "y[c] = kda_ref_bf16_to_double(kda_ref_double_to_bf16(y[c]));   /* hand-off */", ";"),
+    "handoff_g1_not_rounded": (
+        "if (round_g1) g1 = kda_ref_bf16_to_double(kda_ref_double_to_bf16(g1));   /* hand-off */", ";"),
+    "handoff_o_not_rounded": (
+        "o[j] = kda_ref_bf16_to_double(kda_ref_double_to_bf16(o[j]));   /* hand-off */", ";"),
+    "handoff_rounds_k_hat_not_conv_out": (
+        "y[c] = kda_ref_bf16_to_double(kda_ref_double_to_bf16(y[c]));   /* hand-off */",
+        "if (c >= D && c < 2 * D) y[c] = kda_ref_bf16_to_double(kda_ref_double_to_bf16(y[c]));"),
+    "tie_conv_margin_drops_bias": ("double mg = b ? fabs(b[c]) : 0.0;", "double mg = 0.0;"),
+    "tie_g1_certificate_always_exact": ("if (mag == 0.0 || mag <= ldexp(q, 24)) return 0.0;",
+                                        "return 0.0;"),
+    "tie_o_margin_drops_delta_term": ("omag[j] = aq + fabs(beta) * (fabs(v[j]) + ak) * kq;",
+                                      "omag[j] = aq;"),
+    "tie_y_counted_on_wrong_head": ("++p->ties[((int64_t)r * H + h) * 4 + 3];",
+                                    "++p->ties[((int64_t)r * H + 0) * 4 + 3];"),
 }
 
 
