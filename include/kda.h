@@ -68,6 +68,20 @@ typedef enum {
 
 typedef struct kda_handle_s* kda_handle;
 
+/* Where intermediate values are rounded ([kda] module docstring: elementwise
+ * rounding follows the original, unfused path at every bf16 hand-off between
+ * its kernels).
+ *   KDA_ROUND_FUSED         every intermediate stays fp32 inside the kernel;
+ *   KDA_ROUND_BF16_HANDOFF  the values an unfused pipeline hands over in bf16
+ *                           are rounded to bf16 (RNE) where produced: the conv
+ *                           + SiLU outputs q|k|v, g1 = f_b f_a before the gate,
+ *                           and the recurrence output o before the RMSNorm.
+ * The state stays fp32 and core_out bf16 in both modes. */
+typedef enum {
+    KDA_ROUND_FUSED = 0,
+    KDA_ROUND_BF16_HANDOFF = 1
+} kda_rounding;
+
 /* Attention weights of one layer ([prepared] PreparedKda.__init__). Borrowed
  * only during kda_prepare: the library copies and re-lays them out into its
  * own device memory on `hip_stream`; the caller may free them once that
@@ -88,6 +102,7 @@ typedef struct {
     float gate_lower_bound;   /* lb (e.g. -5); finite */
     float norm_eps;           /* o_norm.eps (e.g. 1e-6); >= 0 */
     float l2_eps;             /* epsilon inside the l2norm square root (1e-6); >= 0 */
+    int32_t rounding;         /* a kda_rounding value; zero-initialised = KDA_ROUND_FUSED */
 } kda_weights;
 
 /* The per-slot caches of one layer ([kda] kda_pre launcher: conv_state
@@ -120,7 +135,8 @@ typedef struct {
  * decode_conv_weight) and records the caches. *out is set only on KDA_OK.
  * Errors: KDA_ERR_NULL (w, c, out, a weight or cache pointer), KDA_ERR_SHAPE
  * (heads < 1, num_slots < 1, a stride too small or negative, norm_head_stride
- * not 0 or 128, a non-finite scalar or negative epsilon), KDA_ERR_ALIGN
+ * not 0 or 128, a non-finite scalar or negative epsilon, rounding not a
+ * kda_rounding value), KDA_ERR_ALIGN
  * (state base or stride), KDA_ERR_UNSUPPORTED (conv_width != 4),
  * KDA_ERR_NOMEM, KDA_ERR_HIP. */
 kda_status kda_prepare(const kda_weights* w, const kda_caches* c, void* hip_stream,

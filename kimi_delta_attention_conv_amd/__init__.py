@@ -17,13 +17,15 @@ __all__ = [
     "KdaError", "KdaWeights", "KdaCaches", "load_library", "kda_prepare", "kda_decode",
     "kda_verify", "kda_device_errors", "kda_destroy", "kda_status_string", "KdaCore",
     "kda_linear", "kda_in_proj", "kda_o_proj", "linear",
-    "HEAD_DIM", "FA_RANK", "CONV_WIDTH", "MAX_TOKENS",
+    "HEAD_DIM", "FA_RANK", "CONV_WIDTH", "MAX_TOKENS", "ROUNDING",
 ]
 
 HEAD_DIM = 128
 FA_RANK = 128
 CONV_WIDTH = 4
 MAX_TOKENS = 8
+# kda_rounding: fused (fp32 intermediates) or bf16 at the unfused path's hand-offs
+ROUNDING = {"fused": 0, "bf16_handoff": 1}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
@@ -48,7 +50,7 @@ class KdaWeights(ctypes.Structure):
         ("f_b", ctypes.c_void_p), ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
         ("norm_weight", ctypes.c_void_p), ("norm_head_stride", ctypes.c_int32),
         ("gate_lower_bound", ctypes.c_float), ("norm_eps", ctypes.c_float),
-        ("l2_eps", ctypes.c_float),
+        ("l2_eps", ctypes.c_float), ("rounding", ctypes.c_int32),
     ]
 
 
@@ -199,10 +201,12 @@ class KdaCore:
     Weights: conv_weight bf16 [3D, 1, 4]; conv_bias bf16 [3D] or None; f_b bf16
              [D, 128]; A_log fp32 [H]; dt_bias fp32 [D]; norm_weight fp32 [128]
              or [H, 128].
+    rounding: "fused" (default) or "bf16_handoff" (kda_rounding in kda.h).
     """
 
     def __init__(self, *, conv_weight, conv_bias, f_b, A_log, dt_bias, norm_weight,
-                 gate_lower_bound, norm_eps, conv, state, l2_eps=1e-6, stream=None):
+                 gate_lower_bound, norm_eps, conv, state, l2_eps=1e-6, stream=None,
+                 rounding="fused"):
         import torch
 
         self._torch = torch
@@ -238,7 +242,7 @@ class KdaCore:
                        norm_weight=norm_weight.data_ptr(),
                        norm_head_stride=0 if norm_weight.numel() == HEAD_DIM else HEAD_DIM,
                        gate_lower_bound=float(gate_lower_bound), norm_eps=float(norm_eps),
-                       l2_eps=float(l2_eps))
+                       l2_eps=float(l2_eps), rounding=ROUNDING[rounding])
         cs = conv.stride()
         c = KdaCaches(conv=conv.data_ptr(), conv_slot_stride=cs[0], conv_dim_stride=cs[1],
                       conv_pos_stride=cs[2], state=state.data_ptr(),

@@ -25,6 +25,7 @@ struct kda_handle_s {
     int32_t* err_count = nullptr;
     kda_caches caches{};
     float lb = 0.0f, norm_eps = 0.0f, l2_eps = 0.0f;
+    int32_t rounding = KDA_ROUND_FUSED;
 };
 
 namespace {
@@ -88,6 +89,7 @@ kda::CoreParams core_params(const kda_handle_s* h, const void* projected, int64_
     p.q_scale = 1.0f / std::sqrt((float)kda::kHeadDim);
     p.norm_eps = h->norm_eps;
     p.l2_eps = h->l2_eps;
+    p.handoff_bf16 = h->rounding == KDA_ROUND_BF16_HANDOFF;
     // the dim-first pool [slots][3D][3] with 16-byte aligned slots takes the
     // kernel's coalesced window stores (each head's q, k, v windows are three
     // contiguous 768-byte runs whose starts are multiples of 16 bytes)
@@ -127,6 +129,8 @@ kda_status kda_prepare(const kda_weights* w, const kda_caches* c, void* hip_stre
     if (w->norm_head_stride != 0 && w->norm_head_stride != kda::kHeadDim) return KDA_ERR_SHAPE;
     if (!std::isfinite(w->gate_lower_bound) || !std::isfinite(w->norm_eps) ||
         !std::isfinite(w->l2_eps) || w->norm_eps < 0.0f || w->l2_eps < 0.0f)
+        return KDA_ERR_SHAPE;
+    if (w->rounding != KDA_ROUND_FUSED && w->rounding != KDA_ROUND_BF16_HANDOFF)
         return KDA_ERR_SHAPE;
     const int64_t H = w->heads, D = H * kda::kHeadDim, C = 3 * D;
     if (c->num_slots < 1) return KDA_ERR_SHAPE;
@@ -179,6 +183,7 @@ kda_status kda_prepare(const kda_weights* w, const kda_caches* c, void* hip_stre
     h->lb = w->gate_lower_bound;
     h->norm_eps = w->norm_eps;
     h->l2_eps = w->l2_eps;
+    h->rounding = w->rounding;
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     kda::PrepareParams in{};

@@ -41,6 +41,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// The bf16 value nearest x (ties to even), back in fp32: a bf16 hand-off.
+__device__ __forceinline__ float round_bf16(float x) {
+    return bf16_to_f32(f32_to_bf16(x));
+}
+
 __device__ __forceinline__ float exp_fast(float x) {
     return __builtin_amdgcn_exp2f(x * kLog2e);
 }
@@ -225,7 +230,8 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
             pre = __builtin_fmaf(cw[1], w1, pre);
             pre = __builtin_fmaf(cw[2], w2, pre);
             pre = __builtin_fmaf(cw[3], x, pre);
-            s_qkv[t][cl] = pre * sigmoid(pre);
+            const float y = pre * sigmoid(pre);
+            s_qkv[t][cl] = p.handoff_bf16 ? round_bf16(y) : y;
             w0 = w1; w1 = w2; w2 = x;
             b0 = b1; b1 = b2; b2 = xb[t];
             if (p.conv_dim_first16) {   // staged; written below with 16-byte stores
@@ -256,7 +262,8 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
         for (int i = 0; i < 4; ++i) {
             const int t = 4 * kg + i;
             if (t < L) {
-                const float g = p.lb * sigmoid(aexp * (acc[i] + dtv));
+                const float g1 = p.handoff_bf16 ? round_bf16(acc[i]) : acc[i];
+                const float g = p.lb * sigmoid(aexp * (g1 + dtv));
                 s_eg[t][i_out] = exp_fast(g);
             }
         }
@@ -319,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
                 __builtin_nontemporal_store(S[g][m],
                                             reinterpret_cast<f32x4*>(dp + g * 8 * N + 32 * m));
             }
-            if ((lane & 7) == 0) s_o[t][row] = o;
+            if ((lane & 7) == 0) s_o[t][row] = p.handoff_bf16 ? round_bf16(o) : o;
         }
     }
     __syncthreads();

@@ -38,7 +38,10 @@
  * caller's margin m for a value x (a bound on that implementation's error in
  * x), x counts as a near tie when x - m and x + m round to different bf16
  * values. Margins are relative factors times a magnitude: for a conv output
- * |bias| + sum |w * input|; for g1 sum |f_b f_a| (zero when every term is a
+ * y = SiLU(pre), |SiLU'(pre)| (|bias| + sum |w * input|) + (1 + |pre|) |y| (the
+ * pre-activation's rounding scaled by the slope, plus SiLU's own evaluation,
+ * whose exponential sees an argument rounded relative to |pre|); for g1
+ * sum |f_b f_a| (zero when every term is a
  * multiple of one quantum Q and the sum of |terms| is at most 2^24 Q, where
  * any fp32 summation order is exact); for o the sum over i of |S_dec q_i|
  * plus |beta| (|v| + sum |S_dec k_i|) sum |k_i q_i| (S_dec: the decayed
@@ -360,10 +363,18 @@ int32_t kda_ref_run(const kda_ref_problem* p)
             /* conv update + SiLU over q|k|v; the new window goes to dst[t] */
             if (p->ties && hand)
                 for (int32_t c = 0; c < C; ++c) {
-                    double mg = b ? fabs(b[c]) : 0.0;
-                    for (int32_t m = 0; m < W - 1; ++m)
-                        mg += fabs(w[(int64_t)c * W + m] * win[(int64_t)c * (W - 1) + m]);
-                    cmag[c] = mg + fabs(w[(int64_t)c * W + W - 1] * x[c]);
+                    double mg = b ? fabs(b[c]) : 0.0, pre = b ? b[c] : 0.0;
+                    for (int32_t m = 0; m < W - 1; ++m) {
+                        const double t = w[(int64_t)c * W + m] * win[(int64_t)c * (W - 1) + m];
+                        mg += fabs(t);
+                        pre += t;
+                    }
+                    const double t = w[(int64_t)c * W + W - 1] * x[c];
+                    mg += fabs(t);
+                    pre += t;
+                    const double sg = kda_ref_sigmoid(pre);
+                    const double slope = sg * (1.0 + pre * (1.0 - sg));   /* SiLU'(pre) */
+                    cmag[c] = fabs(slope) * mg + (1.0 + fabs(pre)) * fabs(pre * sg);
                 }
             kda_ref_conv_token(C, W, w, b, win, x, y);
             if (hand)

@@ -29,7 +29,7 @@ class GpuCase:
     """Device copies of a case and a KdaCore bound to them."""
 
     def __init__(self, case: Case, *, projected=None, conv_storage=None, state=None,
-                 norm_weight=None, dt_bias=None, gate_lower_bound=None):
+                 norm_weight=None, dt_bias=None, gate_lower_bound=None, rounding="fused"):
         self.case = case
         self.projected = (case.projected if projected is None else projected).cuda()
         st = case.conv_storage if conv_storage is None else conv_storage
@@ -43,7 +43,8 @@ class GpuCase:
             dt_bias=(case.dt_bias if dt_bias is None else torch.as_tensor(dt_bias)).cuda(),
             norm_weight=(case.norm_weight if norm_weight is None else torch.as_tensor(norm_weight)).cuda(),
             gate_lower_bound=case.gate_lower_bound if gate_lower_bound is None else gate_lower_bound,
-            norm_eps=case.norm_eps, l2_eps=case.l2_eps, conv=self.conv, state=self.state)
+            norm_eps=case.norm_eps, l2_eps=case.l2_eps, conv=self.conv, state=self.state,
+            rounding=rounding)
         self.out = torch.full((case.S, case.D), OUT_SENTINEL, dtype=torch.int16).view(
             torch.bfloat16).cuda()
 

@@ -527,7 +527,8 @@ def _near_ties(x, m):
 
 
 def _conv_outputs(case, conv_slot, x):
-    """SiLU(conv) of one token via torch conv1d, and |bias| + sum |w * input| per channel."""
+    """SiLU(conv) of one token via torch conv1d, and the near-tie magnitude per channel:
+    |SiLU'(pre)| (|bias| + sum |w * input|) + (1 + |pre|) |SiLU(pre)|."""
     D = case.D
     conv0 = om.bf16_bits_to_f64(bf16_np(case.conv_view()))[conv_slot]
     w = om.bf16_bits_to_f64(bf16_np(case.conv_weight))                   # [3D, 1, W]
@@ -537,7 +538,11 @@ def _conv_outputs(case, conv_slot, x):
         torch.from_numpy(seq)[None], torch.from_numpy(w), torch.from_numpy(b),
         groups=3 * D))[0, :, 0].numpy()
     mag = np.abs(b) + np.abs(w[:, 0, :] * seq).sum(1)
-    return y, mag
+    pre = torch.nn.functional.conv1d(torch.from_numpy(seq)[None], torch.from_numpy(w),
+                                     torch.from_numpy(b), groups=3 * D)[0, :, 0].numpy()
+    sg = scipy.special.expit(pre)
+    slope = sg * (1.0 + pre * (1.0 - sg))
+    return y, np.abs(slope) * mag + (1.0 + np.abs(pre)) * np.abs(y)
 
 
 @pin

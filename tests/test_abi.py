@@ -82,6 +82,8 @@ def _caches(**kw):
     (_weights(norm_head_stride=64), _caches(), -2),
     (_weights(norm_eps=float("nan")), _caches(), -2),
     (_weights(l2_eps=-1.0), _caches(), -2),
+    (_weights(rounding=2), _caches(), -2),
+    (_weights(rounding=-1), _caches(), -2),
     (_weights(), _caches(num_slots=0), -2),
     (_weights(), _caches(state_slot_stride=128 * 128), -2),
     (_weights(), _caches(conv_slot_stride=100), -2),

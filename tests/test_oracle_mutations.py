@@ -61,7 +61,8 @@ MUTATIONS = {
     "handoff_rounds_k_hat_not_conv_out": (
         "y[c] = kda_ref_bf16_to_double(kda_ref_double_to_bf16(y[c]));   /* hand-off */",
         "if (c >= D && c < 2 * D) y[c] = kda_ref_bf16_to_double(kda_ref_double_to_bf16(y[c]));"),
-    "tie_conv_margin_drops_bias": ("double mg = b ? fabs(b[c]) : 0.0;", "double mg = 0.0;"),
+    "tie_conv_margin_drops_bias": ("double mg = b ? fabs(b[c]) : 0.0, pre", "double mg = 0.0, pre"),
+    "tie_conv_margin_drops_slope": ("cmag[c] = fabs(slope) * mg +", "cmag[c] = mg +"),
     "tie_g1_certificate_always_exact": ("if (mag == 0.0 || mag <= ldexp(q, 24)) return 0.0;",
                                         "return 0.0;"),
     "tie_o_margin_drops_delta_term": ("omag[j] = aq + fabs(beta) * (fabs(v[j]) + ak) * kq;",
