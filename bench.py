@@ -49,6 +49,8 @@ def parse_args():
     ap.add_argument("--config", type=int, default=3, help="workload 0..4 (default 3)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the oracle baseline (0 disables it)")
+    ap.add_argument("--rounding", choices=("fused", "bf16_handoff"), default="fused",
+                    help="core rounding mode (default fused)")
     ap.add_argument("--probe", action="store_true", help="also run the HBM probes")
     ap.add_argument("--probe-only", action="store_true",
                     help="run only the HBM probes (counter calibration)")
@@ -252,7 +254,7 @@ def main():
                        f_b=case.f_b.to(dev), A_log=case.A_log.to(dev),
                        dt_bias=case.dt_bias.to(dev), norm_weight=case.norm_weight.to(dev),
                        gate_lower_bound=case.gate_lower_bound, norm_eps=case.norm_eps,
-                       l2_eps=case.l2_eps, conv=conv, state=state)
+                       l2_eps=case.l2_eps, conv=conv, state=state, rounding=args.rounding)
     projected = case.projected.to(dev)
     out = torch.empty(case.S, case.D, dtype=torch.bfloat16, device=dev)
     slot_base, views = rotation_sets(case, torch)
@@ -338,6 +340,7 @@ def main():
                    "rows": case.S, "heads": case.H, "head_dim": 128, "pool_slots": case.num_slots,
                    "conv_layout": "dim_first" if case.conv_dim_first else "transposed",
                    "slot_sets_rotated": len(sets), "io": "bf16", "state": "f32",
+                   "rounding": args.rounding,
                    "launch": f"hip_graph x{args.graph}" if args.graph else "eager"},
         "gbps": round(metric_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "metric_bytes_per_step": metric_bytes,
