@@ -21,8 +21,9 @@
 // the K blocks round-robin and their partial tiles are summed through LDS in
 // wave order (a fixed order: results do not depend on timing).
 //
-// Tiled (M > 64): BM x BN tiles with X and W blocks staged through LDS and
-// the next blocks' global loads in flight in register stages.
+// Direct-to-LDS (M > 64, K a multiple of 64): BM x BN tiles, X and W blocks
+// loaded straight into a ring of LDS stages. Tiled (M > 64, other K): the same
+// tiles staged through registers.
 #include "kda_internal.h"
 
 namespace kda {
@@ -261,6 +262,126 @@ __global__ __launch_bounds__(256) void linear_tiled_kernel(const LinearParams p)
         }
 }
 
+// Direct-to-LDS kernel for M > 64 and K a multiple of 64. A workgroup of
+// WGM x WGN waves computes a BM x BN tile; K advances in blocks of 64 through a
+// ring of STAGES LDS buffers that gfx950's global_load_lds_dwordx4 fills without
+// passing through registers, STAGES - 1 blocks ahead of the block multiplied.
+// One explicit vmcnt wait and one barrier per block: register-staged copies
+// made the compiler wait for every load in flight at the loop head, which left
+// each block's global latency exposed.
+//
+// LDS per stage: [BM + BN rows][64 k] bf16 (X rows, then W rows), 128-byte rows
+// without padding. A direct load writes 64 lanes x 16 bytes contiguously, so
+// each wave load fills 8 rows; lane l fetches chunk (l & 7) ^ (l >> 3) of its
+// row, which places chunk c of row r at position c ^ (r & 7). The MFMA
+// fragment reads (16 rows, one chunk each) then hit 16 distinct bank groups.
+template <int BM, int BN, int STAGES, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void linear_lds_kernel(const LinearParams p) {
+    constexpr int WAVES = WGM * WGN;
+    constexpr int ROWS = BM + BN;
+    constexpr int LPB = ROWS / (8 * WAVES);        // direct loads per thread per K block
+    constexpr int TM = BM / WGM / 16, TN = BN / WGN / 16;   // 16 x 16 tiles per wave
+    static_assert(LPB * 8 * WAVES == ROWS, "rows must split into whole wave loads");
+    __shared__ __attribute__((aligned(1024))) uint16_t sm[STAGES][ROWS * 64];
+
+    const int mblocks = (p.M + BM - 1) / BM;
+    const int tiles = mblocks * ((p.N + BN - 1) / BN);
+    int t = blockIdx.x;
+    {
+        const int q = tiles >> 3;
+        if ((int)blockIdx.x < 8 * q) t = (blockIdx.x & 7) * q + (blockIdx.x >> 3);
+    }
+    const int m0 = (t % mblocks) * BM;
+    const int n0 = (t / mblocks) * BN;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int mn = lane & 15, kg = lane >> 4;
+
+    // this lane's global source for load j of a block: row 8 (4 j + wave) + (lane >> 3)
+    // of [A rows; B rows], chunk (lane & 7) ^ (lane >> 3)
+    const uint16_t* src[LPB];
+#pragma unroll
+    for (int j = 0; j < LPB; ++j) {
+        const int row = 8 * (WAVES * j + wave) + (lane >> 3);
+        const int chunk = (lane & 7) ^ (lane >> 3);
+        src[j] = row < BM
+            ? p.X + (int64_t)min(m0 + row, p.M - 1) * p.x_pitch + 8 * chunk
+            : p.W + (int64_t)min(n0 + row - BM, p.N - 1) * p.K + 8 * chunk;
+    }
+    const int nkb = p.K / 64;
+    auto issue = [&](int kb) {
+        const int st = kb % STAGES;
+        const int kk = min(kb, nkb - 1) * 64;     // past the end: a harmless re-read
+#if defined(__HIP_DEVICE_COMPILE__)   // the builtin's LDS operand has no host type
+#pragma unroll
+        for (int j = 0; j < LPB; ++j)
+            __builtin_amdgcn_global_load_lds(src[j] + kk, &sm[st][8 * (WAVES * j + wave) * 64], 16, 0, 0);
+#endif
+    };
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) issue(s);
+    for (int kb = 0; kb < nkb; ++kb) {
+        // block kb has landed once at most (STAGES - 2) blocks of loads are outstanding
+        constexpr int N = (STAGES - 2) * LPB;
+        __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+        // a plain barrier: a fenced one would also wait for the direct loads still
+        // in flight for later blocks; the memory clobber keeps LDS reads and new
+        // direct loads on their side of it
+        __asm__ volatile("s_barrier" ::: "memory");
+        issue(kb + STAGES - 1);                   // into the stage read one block ago
+        const uint16_t* st = sm[kb % STAGES];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            bf16x8 a[TM], b[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = wm * (BM / WGM) + 16 * i + mn;
+                const int pos = (4 * s + kg) ^ (row & 7);
+                a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + row * 64 + 8 * pos));
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int row = BM + wn * (BN / WGN) + 16 * j + mn;
+                const int pos = (4 * s + kg) ^ (row & 7);
+                b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + row * 64 + 8 * pos));
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // no direct load may still target LDS at exit
+
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = n0 + wn * (BN / WGN) + 16 * j + mn;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + wm * (BM / WGM) + 16 * i + 4 * kg + r;
+                if (m < p.M && n < p.N) p.Y[(int64_t)m * p.y_pitch + n] = to_bf16(acc[i][j][r]);
+            }
+        }
+}
+
+template <int BM, int BN, int STAGES, int WGM, int WGN>
+hipError_t launch_lds(const LinearParams& p, hipStream_t s) {
+    const int64_t tiles = (int64_t)((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
+    hipLaunchKernelGGL((linear_lds_kernel<BM, BN, STAGES, WGM, WGN>), dim3((unsigned)tiles),
+                       dim3(64 * WGM * WGN), 0, s, p);
+    return hipGetLastError();
+}
+
 template <int MT, int NT, int WAVES>
 hipError_t launch_skinny(const LinearParams& p, hipStream_t s) {
     const dim3 grid((unsigned)((p.N + 16 * NT - 1) / (16 * NT)), (unsigned)((p.M + 16 * MT - 1) / (16 * MT)));
@@ -279,12 +400,17 @@ hipError_t launch_tiled(const LinearParams& p, hipStream_t s) {
 
 hipError_t launch_linear(const LinearParams& p, hipStream_t s) {
     // shapes measured on MI355X at the projections' sizes (7168 -> 6284,
-    // 1536 -> 7168): 2 column tiles a wave and 8 waves for up to 64 rows,
-    // 128 x 64 LDS tiles with one K block in flight above (deeper register
-    // staging measured no faster)
+    // 1536 -> 7168): 2 column tiles a wave and 8 waves for up to 64 rows; above
+    // that the direct-to-LDS kernel, 128 x 64 tiles of 4 x 2 waves with 4
+    // stages up to 256 rows and 128 x 128 tiles of 2 x 4 waves with 3 stages
+    // beyond; the register-staged kernel only where K is not a multiple of 64
     if (p.M <= 16) return launch_skinny<1, 2, 8>(p, s);
     if (p.M <= 32) return launch_skinny<2, 2, 8>(p, s);
     if (p.M <= 64) return launch_skinny<4, 2, 8>(p, s);
+    if (p.K % 64 == 0) {
+        if (p.M <= 256) return launch_lds<128, 64, 4, 4, 2>(p, s);
+        return launch_lds<128, 128, 3, 2, 4>(p, s);
+    }
     return launch_tiled<128, 64, 2>(p, s);
 }
 

@@ -1,10 +1,13 @@
 """The projection kernel (kda_linear / kda_in_proj / kda_o_proj) vs the oracle.
 
 Bar (derived from the arithmetic): bf16 x bf16 products are exact in fp32, so
-the kernel's only error before the output rounding is fp32 accumulation, at
-most K 2^-24 sum_k |x_k w_k|; the bf16 output adds at most half an ulp, 2^-9
-|y|. Each element must satisfy |y_gpu - y| <= 2^-8 |y| + K 2^-24 sum|x w| with
-y the oracle's double-precision value. Untouched output columns (pitch > N)
+the kernel's only error before the output rounding is fp32 accumulation. The
+matrix cores' internal rounding of their fp32 sums is not specified, and the
+measured errors reach the round-to-nearest bound K 2^-24 sum|x w| (a sign of
+directed rounding), so the bound for directed rounding is used: K 2^-23
+sum_k |x_k w_k|. The bf16 output adds at most half an ulp, 2^-9 |y|. Each
+element must satisfy |y_gpu - y| <= 2^-8 |y| + K 2^-23 sum|x w| with y the
+oracle's double-precision value. Untouched output columns (pitch > N)
 must stay bit-exact, and two runs must agree bit for bit."""
 import numpy as np
 import pytest
@@ -62,7 +65,7 @@ def _check(x, w, got, ms=None, ns=None, label=""):
     absdot = np.einsum("ik,ik->i", np.abs(xf[ms]), np.abs(wf[ns]))
     g = (got[ms, ns].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     err = np.abs(g - ref)
-    lim = 2.0 ** -8 * np.abs(ref) + K * 2.0 ** -24 * absdot
+    lim = 2.0 ** -8 * np.abs(ref) + K * 2.0 ** -23 * absdot
     assert np.all(np.isfinite(g)), label
     worst = float(np.max(err / np.maximum(lim, 1e-300)))
     print(f"[linear] {label}: {ms.size} entries, max err/limit {worst:.3f}, "
@@ -71,7 +74,9 @@ def _check(x, w, got, ms=None, ns=None, label=""):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 8), (5, 37, 136), (16, 16, 128), (17, 33, 264),
-                                   (33, 100, 1024), (64, 48, 520), (70, 129, 384)])
+                                   (33, 100, 1024), (64, 48, 520), (70, 129, 384),
+                                   (100, 77, 520), (256, 65, 64), (257, 130, 192),
+                                   (300, 200, 256)])
 def test_ragged_shapes(M, N, K):
     x, w = make_linear(M, N, K, seed=M * 1000 + N + K, x_pitch=K + 8)
     got = _run(x, w, y_pitch=N + 3)
@@ -79,7 +84,7 @@ def test_ragged_shapes(M, N, K):
     assert np.all(got[:, N:] == SENT), "columns beyond N were written"
 
 
-@pytest.mark.parametrize("rows", [64, 512])
+@pytest.mark.parametrize("rows", [64, 256, 512])
 def test_in_proj_full_shape(rows):
     heads = 12
     N = 4 * 128 * heads + 128 + heads
@@ -92,7 +97,7 @@ def test_in_proj_full_shape(rows):
     assert np.array_equal(got, again), "not deterministic"
 
 
-@pytest.mark.parametrize("rows", [64, 512])
+@pytest.mark.parametrize("rows", [64, 256, 512])
 def test_o_proj_full_shape(rows):
     heads = 12
     x, w = make_linear(rows, HIDDEN, 128 * heads, seed=10 + rows)
