@@ -51,7 +51,9 @@ def parse_args():
                     help="wall-clock budget of the oracle baseline (0 disables it)")
     ap.add_argument("--rounding", choices=("fused", "bf16_handoff"), default="fused",
                     help="core rounding mode (default fused)")
-    ap.add_argument("--probe", action="store_true", help="also run the HBM probes")
+    ap.add_argument("--probe", action="store_true",
+                    help="run the HBM probes (the default; kept for older command lines)")
+    ap.add_argument("--no-probe", action="store_true", help="skip the HBM probes")
     ap.add_argument("--probe-only", action="store_true",
                     help="run only the HBM probes (counter calibration)")
     ap.add_argument("--graph", type=int, default=0, metavar="CHAIN",
@@ -105,8 +107,11 @@ def probe(torch, kda):
         "read": lambda: lib.kda_probe_read(a.data_ptr(), nbytes, sink.data_ptr(), s),
         "write": lambda: lib.kda_probe_write(b.data_ptr(), nbytes, 2.0, s),
         "copy": lambda: lib.kda_probe_copy(b.data_ptr(), a.data_ptr(), nbytes, s),
+        "write_runs": lambda: lib.kda_probe_write_runs(b.data_ptr(), nbytes, 2.0, s),
+        "copy_runs": lambda: lib.kda_probe_copy_runs(b.data_ptr(), a.data_ptr(), nbytes, s),
     }
-    moved = {"read": nbytes, "write": nbytes, "copy": 2 * nbytes}
+    moved = {"read": nbytes, "write": nbytes, "copy": 2 * nbytes, "write_runs": nbytes,
+             "copy_runs": 2 * nbytes}
     res = {}
     for name, fn in calls.items():
         for _ in range(3):
@@ -213,10 +218,50 @@ def cpu_baseline(case, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return dict(value=round(case.S * reps / el, 2), unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{reps} full calls of the same workload ({case.R} requests x {case.L} "
-                       f"tokens x {case.H} heads), single-threaded C oracle in double, "
-                       f"{el:.1f} s")
+    single = case.S * reps / el
+
+    # The same oracle on contiguous chunks of requests, one host thread a chunk:
+    # requests touch disjoint slots, the oracle keeps no global state, and
+    # ctypes releases the interpreter lock during each call.
+    import threading
+    threads = max(1, min(16, os.cpu_count() or 1, case.R))
+    bounds = [case.R * i // threads for i in range(threads + 1)]
+    ss = case.slots_row_stride()
+    done = [0] * threads
+    stop = time.perf_counter() + seconds
+
+    def worker(i):
+        r0, r1 = bounds[i], bounds[i + 1]
+        if r1 == r0:
+            return
+        sub = dict(kw, requests=r1 - r0, projected=kw["projected"][r0 * case.L: r1 * case.L],
+                   slots=flat[r0 * ss: (r1 - 1) * ss + case.L],
+                   accepted=None if kw["accepted"] is None else kw["accepted"][r0:r1],
+                   core_out=out[r0 * case.L: r1 * case.L])
+        while time.perf_counter() < stop:
+            orc.run(**sub)
+            done[i] += (r1 - r0) * case.L
+    t1 = time.perf_counter()
+    pool = [threading.Thread(target=worker, args=(i,)) for i in range(threads)]
+    for t in pool:
+        t.start()
+    for t in pool:
+        t.join()
+    el2 = time.perf_counter() - t1
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return dict(value=round(sum(done) / el2, 2), unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"the same workload ({case.R} requests x {case.L} tokens x {case.H} "
+                       f"heads): {threads} host threads on request chunks for {el2:.1f} s, "
+                       f"and {reps} single-threaded full calls in {el:.1f} s; C oracle in double",
+                single_thread_value=round(single, 2), cpu_model=model,
+                host_cpus=os.cpu_count())
 
 
 def main():
@@ -312,6 +357,39 @@ def main():
     if errors:
         raise RuntimeError(f"{errors} requests were skipped for invalid slots")
 
+    # per-launch distribution (after the timed region): each launch between
+    # its own pair of events on the launch stream
+    launch_us = None
+    hot = None
+    if not args.graph:
+        pairs = []
+        for i in range(50):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launches[i % len(launches)]()
+            b.record(stream)
+            pairs.append((a, b))
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
+        launch_us = {"p10": round(us[4], 2), "p50": round(us[24], 2), "p90": round(us[44], 2),
+                     "launches": len(us)}
+        # hot: the same slot set every step, so part of the pool can stay in the MALL
+        for _ in range(5):
+            launches[0]()
+        torch.cuda.synchronize()
+        h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        h0.record(stream)
+        for _ in range(50):
+            launches[0]()
+        h1.record(stream)
+        torch.cuda.synchronize()
+        hot_ms = h0.elapsed_time(h1) / 50
+        hot = {"kernel_ms": round(hot_ms, 5),
+               "gbps": round((case.R + case.S) * case.H * UNIT_BYTES / (hot_ms * 1e-3) / 1e9, 1),
+               "note": "one slot set every step (reported beside the rotated figure, not as it)"}
+        if core.device_errors():
+            raise RuntimeError("requests were skipped for invalid slots")
+
     per_replay = args.graph if args.graph else 1
     steps_run = args.steps * per_replay
     ms_per_step = wall * 1e3 / steps_run
@@ -349,8 +427,17 @@ def main():
                      "traffic": traffic, "kernel": KERNEL_NAME,
                      "kernel_ms": round(kernel_ms, 5)},
     }
-    if args.probe:
-        result["hbm_probe"] = probe(torch, kda)
+    if launch_us is not None:
+        result["launch_us"] = launch_us
+        result["hot"] = hot
+    if not args.no_probe:
+        print("[bench] HBM probes", file=sys.stderr, flush=True)
+        pr = probe(torch, kda)
+        result["hbm_probe"] = pr
+        best = {"read": pr["read"]["gbps"],
+                "write": max(pr["write"]["gbps"], pr["write_runs"]["gbps"]),
+                "copy": max(pr["copy"]["gbps"], pr["copy_runs"]["gbps"])}
+        result["roofline"]["frac_of_probe"] = {k: round(achieved / v, 4) for k, v in best.items()}
     core.close()
     del state, conv_storage
     torch.cuda.empty_cache()

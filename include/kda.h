@@ -82,6 +82,14 @@ typedef enum {
     KDA_ROUND_BF16_HANDOFF = 1
 } kda_rounding;
 
+/* Element type of the small per-head and per-channel weights (A_log, dt_bias,
+ * norm_weight). The library converts them to fp32 at prepare time ([prepared]
+ * PreparedKda.__init__ casts them to float); bf16 values convert exactly. */
+typedef enum {
+    KDA_F32 = 0,
+    KDA_BF16 = 1
+} kda_dtype;
+
 /* Attention weights of one layer ([prepared] PreparedKda.__init__). Borrowed
  * only during kda_prepare: the library copies and re-lays them out into its
  * own device memory on `hip_stream`; the caller may free them once that
@@ -94,15 +102,19 @@ typedef struct {
                                  ([prepared] decode_conv_weight). 2-byte aligned. */
     const void* conv_bias;    /* bf16 [3D], or NULL for no conv bias (taken as zero) */
     const void* f_b;          /* bf16 [D][128], row i = output channel i. 2-byte aligned. */
-    const float* A_log;       /* fp32 [H], one per head ([prepared]: heads = A_log.numel()) */
-    const float* dt_bias;     /* fp32 [D] */
-    const float* norm_weight; /* fp32 o_norm weight: [128] shared by all heads
-                                 (norm_head_stride 0) or [H][128] (stride 128) */
+    const void* A_log;        /* [H], one per head ([prepared]: heads = A_log.numel());
+                                 element type A_log_dtype */
+    const void* dt_bias;      /* [D]; element type dt_bias_dtype */
+    const void* norm_weight;  /* o_norm weight: [128] shared by all heads (norm_head_stride
+                                 0) or [H][128] (stride 128); element type norm_weight_dtype */
     int32_t norm_head_stride; /* 0 or 128 */
     float gate_lower_bound;   /* lb (e.g. -5); finite */
     float norm_eps;           /* o_norm.eps (e.g. 1e-6); >= 0 */
     float l2_eps;             /* epsilon inside the l2norm square root (1e-6); >= 0 */
     int32_t rounding;         /* a kda_rounding value; zero-initialised = KDA_ROUND_FUSED */
+    int32_t A_log_dtype;      /* kda_dtype of A_log; zero-initialised = KDA_F32 */
+    int32_t dt_bias_dtype;    /* kda_dtype of dt_bias */
+    int32_t norm_weight_dtype;/* kda_dtype of norm_weight */
 } kda_weights;
 
 /* The per-slot caches of one layer ([kda] kda_pre launcher: conv_state
@@ -136,8 +148,9 @@ typedef struct {
  * Errors: KDA_ERR_NULL (w, c, out, a weight or cache pointer), KDA_ERR_SHAPE
  * (heads < 1, num_slots < 1, a stride too small or negative, norm_head_stride
  * not 0 or 128, a non-finite scalar or negative epsilon, rounding not a
- * kda_rounding value), KDA_ERR_ALIGN
- * (state base or stride), KDA_ERR_UNSUPPORTED (conv_width != 4),
+ * kda_rounding value, a dtype not a kda_dtype value), KDA_ERR_ALIGN (a weight
+ * pointer not aligned to its element size, the state base or stride),
+ * KDA_ERR_UNSUPPORTED (conv_width != 4),
  * KDA_ERR_NOMEM, KDA_ERR_HIP. */
 kda_status kda_prepare(const kda_weights* w, const kda_caches* c, void* hip_stream,
                        kda_handle* out);

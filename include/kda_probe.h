@@ -1,11 +1,13 @@
 /*
  * kda_probe.h -- HBM stream probes exported by libkda.so (measurement only).
  *
- * Plain read, write and copy kernels over a device buffer, with the same
- * 16-byte non-temporal accesses the core kernel uses for its state stream.
- * They give the achievable HBM bandwidth on the machine at hand and a kernel
- * of exactly known traffic for calibrating the HBM byte counters (FETCH_SIZE,
- * WRITE_SIZE). They are not part of the KDA method.
+ * Plain read, write and copy kernels over a device buffer. The grid-stride
+ * ones use the same 16-byte non-temporal accesses the core kernel uses for its
+ * state stream and serve as kernels of exactly known traffic for calibrating
+ * the HBM byte counters (FETCH_SIZE, WRITE_SIZE). The _runs variants give each
+ * workgroup one contiguous run with plain stores, the fastest write shape
+ * measured; with the read probe they give the achievable HBM bandwidth on the
+ * machine at hand. None of them is part of the KDA method.
  *
  * All pointers are device pointers, 16-byte aligned; `bytes` is a positive
  * multiple of 16. Calls are asynchronous on `hip_stream`. Return values are
@@ -26,6 +28,11 @@ int kda_probe_copy(void* dst, const void* src, int64_t bytes, void* hip_stream);
 
 /* Fills `bytes` bytes of dst with the fp32 value `value` (writes only). */
 int kda_probe_write(void* dst, int64_t bytes, float value, void* hip_stream);
+
+/* kda_probe_copy and kda_probe_write over one contiguous run per workgroup
+ * (4096 workgroups), plain stores. */
+int kda_probe_copy_runs(void* dst, const void* src, int64_t bytes, void* hip_stream);
+int kda_probe_write_runs(void* dst, int64_t bytes, float value, void* hip_stream);
 
 /* Reads `bytes` bytes of src; writes one fp32 partial sum per workgroup to
  * sink (sink holds at least kda_probe_sink_floats() floats). */

@@ -51,6 +51,8 @@ class KdaWeights(ctypes.Structure):
         ("norm_weight", ctypes.c_void_p), ("norm_head_stride", ctypes.c_int32),
         ("gate_lower_bound", ctypes.c_float), ("norm_eps", ctypes.c_float),
         ("l2_eps", ctypes.c_float), ("rounding", ctypes.c_int32),
+        ("A_log_dtype", ctypes.c_int32), ("dt_bias_dtype", ctypes.c_int32),
+        ("norm_weight_dtype", ctypes.c_int32),
     ]
 
 
@@ -99,7 +101,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_probe_copy.argtypes = [vp, vp, i64, vp]
     lib.kda_probe_write.argtypes = [vp, i64, ctypes.c_float, vp]
     lib.kda_probe_read.argtypes = [vp, i64, vp, vp]
-    for f in (lib.kda_probe_copy, lib.kda_probe_write, lib.kda_probe_read):
+    lib.kda_probe_copy_runs.argtypes = [vp, vp, i64, vp]
+    lib.kda_probe_write_runs.argtypes = [vp, i64, ctypes.c_float, vp]
+    for f in (lib.kda_probe_copy, lib.kda_probe_write, lib.kda_probe_read, lib.kda_probe_copy_runs,
+              lib.kda_probe_write_runs):
         f.restype = ctypes.c_int
     lib.kda_probe_sink_floats.argtypes = []
     lib.kda_probe_sink_floats.restype = i32
@@ -199,8 +204,8 @@ class KdaCore:
              first, or the transposed view of [slots, 3, 3D] storage).
     state  : fp32 [slots, H, 128, 128] (slot stride may exceed H*128*128).
     Weights: conv_weight bf16 [3D, 1, 4]; conv_bias bf16 [3D] or None; f_b bf16
-             [D, 128]; A_log fp32 [H]; dt_bias fp32 [D]; norm_weight fp32 [128]
-             or [H, 128].
+             [D, 128]; A_log [H], dt_bias [D], norm_weight [128] or [H, 128], each
+             fp32 or bf16 (converted to fp32 at prepare time).
     rounding: "fused" (default) or "bf16_handoff" (kda_rounding in kda.h).
     """
 
@@ -213,12 +218,14 @@ class KdaCore:
         H = int(A_log.numel())
         D = H * HEAD_DIM
         for name, t, dt in (("conv_weight", conv_weight, torch.bfloat16),
-                            ("f_b", f_b, torch.bfloat16), ("A_log", A_log, torch.float32),
-                            ("dt_bias", dt_bias, torch.float32),
-                            ("norm_weight", norm_weight, torch.float32),
+                            ("f_b", f_b, torch.bfloat16),
                             ("conv", conv, torch.bfloat16), ("state", state, torch.float32)):
             if t.dtype != dt or not t.is_cuda:
                 raise TypeError(f"{name} must be a {dt} device tensor")
+        small_dtypes = {torch.float32: 0, torch.bfloat16: 1}   # kda_dtype
+        for name, t in (("A_log", A_log), ("dt_bias", dt_bias), ("norm_weight", norm_weight)):
+            if t.dtype not in small_dtypes or not t.is_cuda:
+                raise TypeError(f"{name} must be a float32 or bfloat16 device tensor")
         if conv_bias is not None and (conv_bias.dtype != torch.bfloat16 or not conv_bias.is_cuda):
             raise TypeError("conv_bias must be a bfloat16 device tensor or None")
         for name, t in (("conv_weight", conv_weight), ("f_b", f_b), ("A_log", A_log),
@@ -242,7 +249,9 @@ class KdaCore:
                        norm_weight=norm_weight.data_ptr(),
                        norm_head_stride=0 if norm_weight.numel() == HEAD_DIM else HEAD_DIM,
                        gate_lower_bound=float(gate_lower_bound), norm_eps=float(norm_eps),
-                       l2_eps=float(l2_eps), rounding=ROUNDING[rounding])
+                       l2_eps=float(l2_eps), rounding=ROUNDING[rounding],
+                       A_log_dtype=small_dtypes[A_log.dtype], dt_bias_dtype=small_dtypes[dt_bias.dtype],
+                       norm_weight_dtype=small_dtypes[norm_weight.dtype])
         cs = conv.stride()
         c = KdaCaches(conv=conv.data_ptr(), conv_slot_stride=cs[0], conv_dim_stride=cs[1],
                       conv_pos_stride=cs[2], state=state.data_ptr(),

@@ -1,6 +1,8 @@
 // HBM stream probes (measurement only; see include/kda_probe.h): grid-stride
 // read, write and copy with 16-byte non-temporal accesses, sized to keep every
-// CU's memory pipeline busy (256 CUs x 8 workgroups of 256 threads).
+// CU's memory pipeline busy (256 CUs x 8 workgroups of 256 threads), and write
+// and copy over one contiguous run per workgroup with plain stores (4096
+// workgroups of 256 threads), the fastest write shape measured on MI355X.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -50,6 +52,25 @@ __global__ __launch_bounds__(kThreads) void probe_read(const f32x4* __restrict__
     }
 }
 
+// Workgroup b covers float4 elements [b * per, min((b + 1) * per, n)).
+__global__ __launch_bounds__(kThreads) void probe_write_runs(f32x4* __restrict__ dst, int64_t n,
+                                                             int64_t per, float value) {
+    const f32x4 v = {value, value, value, value};
+    const int64_t lo = (int64_t)blockIdx.x * per;
+    const int64_t hi = lo + per < n ? lo + per : n;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += kThreads) dst[i] = v;
+}
+
+__global__ __launch_bounds__(kThreads) void probe_copy_runs(f32x4* __restrict__ dst,
+                                                            const f32x4* __restrict__ src,
+                                                            int64_t n, int64_t per) {
+    const int64_t lo = (int64_t)blockIdx.x * per;
+    const int64_t hi = lo + per < n ? lo + per : n;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += kThreads) dst[i] = src[i];
+}
+
+constexpr int kRunBlocks = 4096;
+
 bool ok16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 int launched() { return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
@@ -75,6 +96,26 @@ int kda_probe_write(void* dst, int64_t bytes, float value, void* hip_stream) {
     hipLaunchKernelGGL(probe_write, dim3(kBlocks), dim3(kThreads), 0,
                        static_cast<hipStream_t>(hip_stream), static_cast<f32x4*>(dst), bytes / 16,
                        value);
+    return launched();
+}
+
+int kda_probe_write_runs(void* dst, int64_t bytes, float value, void* hip_stream) {
+    if (dst == nullptr) return KDA_ERR_NULL;
+    if (bytes <= 0 || bytes % 16 != 0 || !ok16(dst)) return KDA_ERR_ALIGN;
+    const int64_t n = bytes / 16, per = (n + kRunBlocks - 1) / kRunBlocks;
+    hipLaunchKernelGGL(probe_write_runs, dim3(kRunBlocks), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(hip_stream), static_cast<f32x4*>(dst), n, per,
+                       value);
+    return launched();
+}
+
+int kda_probe_copy_runs(void* dst, const void* src, int64_t bytes, void* hip_stream) {
+    if (dst == nullptr || src == nullptr) return KDA_ERR_NULL;
+    if (bytes <= 0 || bytes % 16 != 0 || !ok16(dst) || !ok16(src)) return KDA_ERR_ALIGN;
+    const int64_t n = bytes / 16, per = (n + kRunBlocks - 1) / kRunBlocks;
+    hipLaunchKernelGGL(probe_copy_runs, dim3(kRunBlocks), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(hip_stream), static_cast<f32x4*>(dst),
+                       static_cast<const f32x4*>(src), n, per);
     return launched();
 }
 

@@ -132,6 +132,8 @@ kda_status kda_prepare(const kda_weights* w, const kda_caches* c, void* hip_stre
         return KDA_ERR_SHAPE;
     if (w->rounding != KDA_ROUND_FUSED && w->rounding != KDA_ROUND_BF16_HANDOFF)
         return KDA_ERR_SHAPE;
+    for (int32_t dt : {w->A_log_dtype, w->dt_bias_dtype, w->norm_weight_dtype})
+        if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_SHAPE;
     const int64_t H = w->heads, D = H * kda::kHeadDim, C = 3 * D;
     if (c->num_slots < 1) return KDA_ERR_SHAPE;
     if (c->conv_slot_stride < 0 || c->conv_dim_stride < 0 || c->conv_pos_stride < 0)
@@ -143,8 +145,10 @@ kda_status kda_prepare(const kda_weights* w, const kda_caches* c, void* hip_stre
     if (c->state_slot_stride < H * kda::kHeadDim * kda::kHeadDim) return KDA_ERR_SHAPE;
     if (c->state_slot_stride % 4 != 0 || !aligned(c->state, 16)) return KDA_ERR_ALIGN;
     if (!aligned(c->conv, 2) || !aligned(w->conv_weight, 2) || !aligned(w->f_b, 2) ||
-        (w->conv_bias != nullptr && !aligned(w->conv_bias, 2)) || !aligned(w->A_log, 4) ||
-        !aligned(w->dt_bias, 4) || !aligned(w->norm_weight, 4))
+        (w->conv_bias != nullptr && !aligned(w->conv_bias, 2)) ||
+        !aligned(w->A_log, w->A_log_dtype == KDA_BF16 ? 2 : 4) ||
+        !aligned(w->dt_bias, w->dt_bias_dtype == KDA_BF16 ? 2 : 4) ||
+        !aligned(w->norm_weight, w->norm_weight_dtype == KDA_BF16 ? 2 : 4))
         return KDA_ERR_ALIGN;
 
     kda_handle_s* h = new (std::nothrow) kda_handle_s();
@@ -195,6 +199,9 @@ kda_status kda_prepare(const kda_weights* w, const kda_caches* c, void* hip_stre
     in.norm_weight = w->norm_weight;
     in.norm_head_stride = w->norm_head_stride;
     in.heads = w->heads;
+    in.A_log_bf16 = w->A_log_dtype == KDA_BF16;
+    in.dt_bias_bf16 = w->dt_bias_dtype == KDA_BF16;
+    in.norm_weight_bf16 = w->norm_weight_dtype == KDA_BF16;
     e = hipMemsetAsync(h->err_count, 0, sizeof(int32_t), s);
     if (e == hipSuccess) e = kda::launch_prepare(in, h->w, s);
     if (e != hipSuccess) {

@@ -361,10 +361,15 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
     }
 }
 
+// Element i of a small weight given as bf16 or fp32.
+__device__ __forceinline__ float load_weight(const void* p, int64_t i, bool bf16) {
+    return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
+}
+
 // Weight re-layout at prepare time ([prepared] PreparedKda.__init__ and
 // decode_conv_weight): conv weight [3D][1][W] -> fp32 [3][W][D], bias -> fp32
-// (zeros if absent), f_b copied, A_log -> exp(A_log), dt_bias copied, norm
-// weight expanded to [H][128]. One grid-stride pass over all items.
+// (zeros if absent), f_b copied, A_log -> exp(A_log), dt_bias -> fp32, norm
+// weight expanded to fp32 [H][128]. One grid-stride pass over all items.
 __global__ void kda_prepare_kernel(const PrepareParams in, const PreparedWeights out) {
     const int64_t H = in.heads, D = H * kHeadDim, C = 3 * D;
     const int64_t n_w = C * kWidth, n_b = C, n_fb = D * kFaRank, n_a = H, n_dt = D,
@@ -390,16 +395,17 @@ __global__ void kda_prepare_kernel(const PrepareParams in, const PreparedWeights
         }
         i -= n_fb;
         if (i < n_a) {
-            out.a_exp[i] = expf(in.A_log[i]);
+            out.a_exp[i] = expf(load_weight(in.A_log, i, in.A_log_bf16));
             continue;
         }
         i -= n_a;
         if (i < n_dt) {
-            out.dt_bias[i] = in.dt_bias[i];
+            out.dt_bias[i] = load_weight(in.dt_bias, i, in.dt_bias_bf16);
             continue;
         }
         i -= n_dt;
-        out.norm_w[i] = in.norm_weight[(i / kHeadDim) * in.norm_head_stride + i % kHeadDim];
+        out.norm_w[i] = load_weight(in.norm_weight, (i / kHeadDim) * in.norm_head_stride + i % kHeadDim,
+                                    in.norm_weight_bf16);
     }
 }
 

@@ -58,11 +58,12 @@ struct PrepareParams {
     const uint16_t* conv_weight;  // bf16 [3D][1][W]
     const uint16_t* conv_bias;    // bf16 [3D] or nullptr
     const uint16_t* f_b;          // bf16 [D][128]
-    const float* A_log;           // [H]
-    const float* dt_bias;         // [D]
-    const float* norm_weight;     // [128] or [H][128]
+    const void* A_log;            // [H]
+    const void* dt_bias;          // [D]
+    const void* norm_weight;      // [128] or [H][128]
     int32_t norm_head_stride;
     int32_t heads;
+    int32_t A_log_bf16, dt_bias_bf16, norm_weight_bf16;   // element type bf16 (else fp32)
 };
 
 // Y[M][N] = X[M][K] W[N][K]^T (bf16 in, fp32 accumulate, bf16 out).

@@ -91,6 +91,10 @@ def _caches(**kw):
     (_weights(), _caches(state=0x40004), -3),
     (_weights(), _caches(state_slot_stride=2 * 128 * 128 + 2), -3),
     (_weights(A_log=0x10002), _caches(), -3),
+    (_weights(dt_bias=0x10001, dt_bias_dtype=1), _caches(), -3),
+    (_weights(norm_weight=0x10002, norm_weight_dtype=0), _caches(), -3),
+    (_weights(A_log_dtype=2), _caches(), -2),
+    (_weights(norm_weight_dtype=-1), _caches(), -2),
 ], ids=lambda v: str(v) if isinstance(v, int) else "")
 def test_prepare_validation_without_gpu(lib, weights, caches, status):
     h = ctypes.c_void_p()
@@ -104,6 +108,8 @@ def test_probe_validation_without_gpu(lib):
     assert lib.kda_probe_copy(None, 0x1000, 16, None) == -1
     assert lib.kda_probe_write(0x1008, 16, 1.0, None) == -3
     assert lib.kda_probe_read(0x1000, 24, 0x2000, None) == -3
+    assert lib.kda_probe_copy_runs(0x1000, None, 16, None) == -1
+    assert lib.kda_probe_write_runs(0x1000, 20, 1.0, None) == -3
     assert lib.kda_probe_sink_floats() > 0
 
 

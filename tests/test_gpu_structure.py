@@ -255,3 +255,24 @@ def test_conv_fast_and_generic_store_paths_agree():
         results.append((conv.cpu().view(torch.int16), state.cpu(), out.cpu().view(torch.int16)))
     for a, b in zip(results[0], results[1]):
         assert torch.equal(a, b)
+
+
+def test_bf16_small_weights_equal_fp32_bit_exact():
+    """A_log, dt_bias and the norm weight given as bf16 are converted at prepare time:
+    the results equal those from fp32 tensors holding the same values, bit for bit,
+    and meet the oracle's bars."""
+    import dataclasses
+    from gpu_cases import run_gpu
+    base = make_case(8, 3, 4, 64, seed=940, verify=True)
+    rounded = dataclasses.replace(
+        base, A_log=base.A_log.to(torch.bfloat16).float(),
+        dt_bias=base.dt_bias.to(torch.bfloat16).float(),
+        norm_weight=base.norm_weight.to(torch.bfloat16).float())
+    as_bf16 = dataclasses.replace(
+        rounded, A_log=rounded.A_log.to(torch.bfloat16), dt_bias=rounded.dt_bias.to(torch.bfloat16),
+        norm_weight=rounded.norm_weight.to(torch.bfloat16))
+    f32 = run_gpu(rounded)
+    b16 = run_gpu(as_bf16)
+    for key in ("out", "conv", "state"):
+        assert np.array_equal(f32[key], b16[key]), key
+    assert_parity(rounded, run_oracle(rounded), b16, rounded.state.numpy(), label="bf16 small weights")
