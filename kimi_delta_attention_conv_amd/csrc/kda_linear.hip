@@ -275,9 +275,14 @@ __global__ __launch_bounds__(256) void linear_tiled_kernel(const LinearParams p)
 // each wave load fills 8 rows; lane l fetches chunk (l & 7) ^ (l >> 3) of its
 // row, which places chunk c of row r at position c ^ (r & 7). The MFMA
 // fragment reads (16 rows, one chunk each) then hit 16 distinct bank groups.
-template <int BM, int BN, int STAGES, int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN) void linear_lds_kernel(const LinearParams p) {
-    constexpr int WAVES = WGM * WGN;
+//
+// With KS = 2 the waves form two groups that take the two 32-wide halves of
+// every K block (each wave's fragment reads per block halve while its tile
+// stays large); the groups' partial tiles are summed through LDS at the end.
+template <int BM, int BN, int STAGES, int WGM, int WGN, int KS>
+__global__ __launch_bounds__(64 * WGM * WGN * KS) void linear_lds_kernel(const LinearParams p) {
+    static_assert(KS == 1 || KS == 2, "K split of a 64-wide block into 1 or 2 parts");
+    constexpr int WAVES = WGM * WGN * KS;
     constexpr int ROWS = BM + BN;
     constexpr int LPB = ROWS / (8 * WAVES);        // direct loads per thread per K block
     constexpr int TM = BM / WGM / 16, TN = BN / WGN / 16;   // 16 x 16 tiles per wave
@@ -294,7 +299,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_lds_kernel(const Linear
     const int m0 = (t % mblocks) * BM;
     const int n0 = (t / mblocks) * BN;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave / WGN, wn = wave % WGN;
+    const int kh = wave / (WGM * WGN);            // K part of this wave's group
+    const int slot = wave % (WGM * WGN);          // tile position within the group
+    const int wm = slot / WGN, wn = slot % WGN;
     const int mn = lane & 15, kg = lane >> 4;
 
     // this lane's global source for load j of a block: row 8 (4 j + wave) + (lane >> 3)
@@ -338,7 +345,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_lds_kernel(const Linear
         issue(kb + STAGES - 1);                   // into the stage read one block ago
         const uint16_t* st = sm[kb % STAGES];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s = kh * (2 / KS); s < (kh + 1) * (2 / KS); ++s) {
             bf16x8 a[TM], b[TN];
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
@@ -361,6 +368,30 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_lds_kernel(const Linear
     }
     __builtin_amdgcn_s_waitcnt(0);   // no direct load may still target LDS at exit
 
+    if (KS == 2) {   // group 1 parks its tiles in the (now idle) stages, group 0 adds them
+        static_assert(KS == 1 || WGM * WGN * TM * TN * 256 * 4 <= (int)sizeof(sm), "room to reduce");
+        float* red = reinterpret_cast<float*>(&sm[0][0]);
+        __syncthreads();
+        if (kh == 1) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        red[((slot * TM + i) * TN + j) * 256 + r * 64 + lane] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (kh == 1) return;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[i][j][r] += red[((slot * TM + i) * TN + j) * 256 + r * 64 + lane];
+    }
+
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -374,11 +405,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void linear_lds_kernel(const Linear
         }
 }
 
-template <int BM, int BN, int STAGES, int WGM, int WGN>
+template <int BM, int BN, int STAGES, int WGM, int WGN, int KS>
 hipError_t launch_lds(const LinearParams& p, hipStream_t s) {
     const int64_t tiles = (int64_t)((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
-    hipLaunchKernelGGL((linear_lds_kernel<BM, BN, STAGES, WGM, WGN>), dim3((unsigned)tiles),
-                       dim3(64 * WGM * WGN), 0, s, p);
+    hipLaunchKernelGGL((linear_lds_kernel<BM, BN, STAGES, WGM, WGN, KS>), dim3((unsigned)tiles),
+                       dim3(64 * WGM * WGN * KS), 0, s, p);
     return hipGetLastError();
 }
 
@@ -402,14 +433,15 @@ hipError_t launch_linear(const LinearParams& p, hipStream_t s) {
     // shapes measured on MI355X at the projections' sizes (7168 -> 6284,
     // 1536 -> 7168): 2 column tiles a wave and 8 waves for up to 64 rows; above
     // that the direct-to-LDS kernel, 128 x 64 tiles of 4 x 2 waves with 4
-    // stages up to 256 rows and 128 x 128 tiles of 2 x 4 waves with 3 stages
-    // beyond; the register-staged kernel only where K is not a multiple of 64
+    // stages up to 256 rows and 128 x 128 tiles of 2 x 4 waves per K half (16
+    // waves) with 3 stages beyond; the register-staged kernel only where K is
+    // not a multiple of 64
     if (p.M <= 16) return launch_skinny<1, 2, 8>(p, s);
     if (p.M <= 32) return launch_skinny<2, 2, 8>(p, s);
     if (p.M <= 64) return launch_skinny<4, 2, 8>(p, s);
     if (p.K % 64 == 0) {
-        if (p.M <= 256) return launch_lds<128, 64, 4, 4, 2>(p, s);
-        return launch_lds<128, 128, 3, 2, 4>(p, s);
+        if (p.M <= 256) return launch_lds<128, 64, 4, 4, 2, 1>(p, s);
+        return launch_lds<128, 128, 3, 2, 4, 2>(p, s);
     }
     return launch_tiled<128, 64, 2>(p, s);
 }

@@ -1,13 +1,15 @@
 """The projection kernel (kda_linear / kda_in_proj / kda_o_proj) vs the oracle.
 
 Bar (derived from the arithmetic): bf16 x bf16 products are exact in fp32, so
-the kernel's only error before the output rounding is fp32 accumulation. The
-matrix cores' internal rounding of their fp32 sums is not specified, and the
-measured errors reach the round-to-nearest bound K 2^-24 sum|x w| (a sign of
-directed rounding), so the bound for directed rounding is used: K 2^-23
-sum_k |x_k w_k|. The bf16 output adds at most half an ulp, 2^-9 |y|. Each
-element must satisfy |y_gpu - y| <= 2^-8 |y| + K 2^-23 sum|x w| with y the
-oracle's double-precision value. Untouched output columns (pitch > N)
+the kernel's only error before the output rounding is fp32 accumulation, at
+most K u sum_k |x_k w_k| with u = 2^-24 for round-to-nearest sums. The matrix
+cores' internal rounding of their fp32 sums is not documented, so u = 2^-23
+(the unit of directed rounding) is used; it also covers the accumulation
+error's share of the output rounding. The bf16 output adds at most half an
+ulp, which is up to 2^-8 |y| when |y| lies just above a power of two (so
+measured ratios near 1 come from the output rounding). Each element must
+satisfy |y_gpu - y| <= 2^-8 |y| + K 2^-23 sum|x w| with y the oracle's
+double-precision value. Untouched output columns (pitch > N)
 must stay bit-exact, and two runs must agree bit for bit."""
 import numpy as np
 import pytest
