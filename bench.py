@@ -59,6 +59,8 @@ def parse_args():
     ap.add_argument("--graph", type=int, default=0, metavar="CHAIN",
                     help="capture CHAIN consecutive launches (rotating slot sets) in one HIP "
                          "graph and time graph replays (steps rounded up to whole replays)")
+    ap.add_argument("--layer", action="store_true",
+                    help="time in_proj -> core -> o_proj per step instead (eager and one HIP graph)")
     ap.add_argument("--proj", action="store_true",
                     help="time the in_proj / o_proj projections at the workload's row count "
                          "instead of the core (prints one JSON line)")
@@ -182,6 +184,109 @@ def bench_projections(args, torch, kda):
     return out
 
 
+def bench_layer(args, torch, kda):
+    """One layer's attention-core step as a serving loop runs it: in_proj
+    (hidden 7168 -> packed row), the core (decode or verify), o_proj (D -> 7168).
+    Weight copies and slot sets rotate so that every step streams from HBM."""
+    from kda_inputs import HIDDEN, make_config, make_linear
+    case = make_config(args.config)
+    S, H, D, pitch = case.S, case.H, case.D, case.pitch
+    n_in = 4 * D + 128 + H
+    lib = kda.load_library()
+    dev = "cuda"
+    x, w_in = make_linear(S, n_in, HIDDEN, seed=21)
+    _, w_o = make_linear(1, HIDDEN, D, seed=22)
+    copies = 4
+    xs = x.to(dev)
+    w_ins = [w_in.to(dev) for _ in range(copies)]
+    w_os = [w_o.to(dev) for _ in range(copies)]
+    conv_storage = case.conv_storage.to(dev)
+    conv = conv_storage if case.conv_dim_first else conv_storage.transpose(-1, -2)
+    state = case.state.to(dev)
+    core = kda.KdaCore(conv_weight=case.conv_weight.to(dev),
+                       conv_bias=None if case.conv_bias is None else case.conv_bias.to(dev),
+                       f_b=case.f_b.to(dev), A_log=case.A_log.to(dev), dt_bias=case.dt_bias.to(dev),
+                       norm_weight=case.norm_weight.to(dev), gate_lower_bound=case.gate_lower_bound,
+                       norm_eps=case.norm_eps, l2_eps=case.l2_eps, conv=conv, state=state)
+    projected = torch.zeros(S, pitch, dtype=torch.bfloat16, device=dev)
+    core_out = torch.empty(S, D, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(S, HIDDEN, dtype=torch.bfloat16, device=dev)
+    slot_base, views = rotation_sets(case, torch)
+    slot_base = slot_base.to(dev)
+    sets = [torch.as_strided(slot_base, sh, st, off) for sh, st, off in views]
+    accepted = None if case.accepted is None else case.accepted.to(dev)
+    h = core.handle
+
+    def parts(i, sp):
+        w1, w2, sl = w_ins[i % copies], w_os[i % copies], sets[i % len(sets)]
+        return [
+            lambda: lib.kda_in_proj(xs.data_ptr(), HIDDEN, w1.data_ptr(), projected.data_ptr(),
+                                    pitch, S, HIDDEN, H, sp),
+            (lambda: lib.kda_decode(h, projected.data_ptr(), pitch, case.R, sl.data_ptr(),
+                                    core_out.data_ptr(), sp)) if accepted is None else
+            (lambda: lib.kda_verify(h, projected.data_ptr(), pitch, case.R, case.L, sl.data_ptr(),
+                                    sl.stride(0), accepted.data_ptr(), core_out.data_ptr(), sp)),
+            lambda: lib.kda_o_proj(core_out.data_ptr(), D, w2.data_ptr(), out.data_ptr(), HIDDEN,
+                                   S, H, HIDDEN, sp),
+        ]
+
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    steps, warm = args.steps, args.warmup
+    for i in range(warm):
+        for f in parts(i, sp):
+            assert f() == 0
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        for f in parts(i, sp):
+            f()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) / steps * 1e3
+    # each kernel alone (its own events), same rotation
+    names = ("in_proj", "core", "o_proj")
+    alone = {}
+    for k, name in enumerate(names):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(steps):
+            parts(i, sp)[k]()
+        b.record(stream)
+        torch.cuda.synchronize()
+        alone[name] = round(a.elapsed_time(b) / steps * 1e3, 2)
+    # one HIP graph holding `copies` whole steps (every weight copy once)
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        spc = torch.cuda.current_stream().cuda_stream
+        for i in range(copies):
+            for f in parts(i, spc):
+                if f() != 0:
+                    raise RuntimeError("capture failed")
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // copies)
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_us = g0.elapsed_time(g1) / (reps * copies) * 1e3
+    errors = core.device_errors()
+    core.close()
+    if errors:
+        raise RuntimeError(f"{errors} requests were skipped")
+    return {"workload": case.name, "rows": S, "heads": H, "hidden": HIDDEN,
+            "eager_us_per_step": round(eager_us, 2), "graph_us_per_step": round(graph_us, 2),
+            "tokens_per_s_graph": round(S / (graph_us * 1e-6), 1),
+            "kernel_us_alone": alone, "weight_copies_rotated": copies,
+            "note": "synthetic weights; the core's inputs are in_proj's outputs"}
+
+
 def cpu_baseline(case, seconds):
     """The oracle, as it stands, timed on the host on the same workload."""
     import numpy as np
@@ -283,6 +388,9 @@ def main():
 
     if args.probe_only:
         print(json.dumps({"hbm_probe": probe(torch, kda)}), flush=True)
+        return
+    if args.layer:
+        print(json.dumps({"layer": bench_layer(args, torch, kda)}), flush=True)
         return
     if args.proj:
         print(json.dumps({"projections": bench_projections(args, torch, kda),
