@@ -9,20 +9,20 @@
 //   docstring and stage_o: o_proj over the core rows (K = 1536 local), an
 //   MFMA GEMV with the token dimension padded to 16.
 //
-// Two kernels, chosen by the row count M:
+// Three kernels, chosen by the row count M and K:
 //
-// Skinny (M <= 64, decode-sized): both operands are K-contiguous (rows of X,
-// rows of the nn.Linear weight W), so every lane reads 64 contiguous bytes of
-// one row per 128-wide K block and feeds v_mfma_f32_16x16x32_bf16 directly
-// from registers. Within a K block, lane group kg (= lane >> 4) hands K
-// elements 8 (kg + 4q) .. +8 to MFMA K step q; A and B use the same
-// assignment, so the product is unchanged. A
+// Skinny (M <= 16, and up to 64 rows when K is not a multiple of 64): both
+// operands are K-contiguous (rows of X, rows of the nn.Linear weight W), so
+// every lane reads 64 contiguous bytes of one row per 128-wide K block and
+// feeds v_mfma_f32_16x16x32_bf16 directly from registers. Within a K block,
+// lane group kg (= lane >> 4) hands K elements 8 (kg + 4q) .. +8 to MFMA K
+// step q; A and B use the same assignment, so the product is unchanged. A
 // workgroup computes 16 * NT output columns for 16 * MT rows; its waves take
 // the K blocks round-robin and their partial tiles are summed through LDS in
 // wave order (a fixed order: results do not depend on timing).
 //
-// Direct-to-LDS (M > 64, K a multiple of 64): BM x BN tiles, X and W blocks
-// loaded straight into a ring of LDS stages. Tiled (M > 64, other K): the same
+// Direct-to-LDS (M > 16, K a multiple of 64): BM x BN tiles, X and W blocks
+// loaded straight into a ring of LDS stages. Tiled (M > 64, other K): 128 x 64
 // tiles staged through registers.
 #include "kda_internal.h"
 
@@ -431,18 +431,22 @@ hipError_t launch_tiled(const LinearParams& p, hipStream_t s) {
 
 hipError_t launch_linear(const LinearParams& p, hipStream_t s) {
     // shapes measured on MI355X at the projections' sizes (7168 -> 6284,
-    // 1536 -> 7168): 2 column tiles a wave and 8 waves for up to 64 rows; above
-    // that the direct-to-LDS kernel, 128 x 64 tiles of 4 x 2 waves with 4
-    // stages up to 256 rows and 128 x 128 tiles of 2 x 4 waves per K half (16
-    // waves) with 3 stages beyond; the register-staged kernel only where K is
-    // not a multiple of 64
+    // 1536 -> 7168). Up to 16 rows the skinny kernel (2 column tiles a wave, 8
+    // waves). Above that the direct-to-LDS kernel: 32 x 32 tiles with 8 stages
+    // up to 32 rows and 32 x 64 tiles with 6 stages up to 64 (two waves, or two
+    // pairs, on the two K halves of each block); 128 x 64 tiles of 4 x 2 waves
+    // with 4 stages up to 256 rows; 128 x 128 tiles of 2 x 4 waves per K half
+    // (16 waves) with 3 stages beyond. K not a multiple of 64 takes the skinny
+    // kernel up to 64 rows and the register-staged kernel above.
     if (p.M <= 16) return launch_skinny<1, 2, 8>(p, s);
-    if (p.M <= 32) return launch_skinny<2, 2, 8>(p, s);
-    if (p.M <= 64) return launch_skinny<4, 2, 8>(p, s);
     if (p.K % 64 == 0) {
+        if (p.M <= 32) return launch_lds<32, 32, 8, 1, 1, 2>(p, s);
+        if (p.M <= 64) return launch_lds<32, 64, 6, 1, 2, 2>(p, s);
         if (p.M <= 256) return launch_lds<128, 64, 4, 4, 2, 1>(p, s);
         return launch_lds<128, 128, 3, 2, 4, 2>(p, s);
     }
+    if (p.M <= 32) return launch_skinny<2, 2, 8>(p, s);
+    if (p.M <= 64) return launch_skinny<4, 2, 8>(p, s);
     return launch_tiled<128, 64, 2>(p, s);
 }
 

@@ -78,7 +78,7 @@ def _check(x, w, got, ms=None, ns=None, label=""):
 @pytest.mark.parametrize("M,N,K", [(1, 1, 8), (5, 37, 136), (16, 16, 128), (17, 33, 264),
                                    (33, 100, 1024), (64, 48, 520), (70, 129, 384),
                                    (100, 77, 520), (256, 65, 64), (257, 130, 192),
-                                   (300, 200, 256)])
+                                   (300, 200, 256), (20, 45, 128), (40, 65, 192), (17, 31, 64)])
 def test_ragged_shapes(M, N, K):
     x, w = make_linear(M, N, K, seed=M * 1000 + N + K, x_pitch=K + 8)
     got = _run(x, w, y_pitch=N + 3)
