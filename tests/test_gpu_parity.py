@@ -80,3 +80,27 @@ def test_chained_verify_steps():
             g.conv_storage.copy_(conv)
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("variant", ["saturated", "strong_decay_large_inputs"])
+def test_extreme_parameters(variant):
+    """Saturating and extreme values: a gate sigmoid driven far into saturation
+    (A_log up to 4, so exp(A_log) ~ 55), a lower bound of -30 (decays down to
+    e^-30 per token over 8 tokens), beta_raw ~ N(0, 4^2) (beta near 0 or 1), and
+    inputs 4x larger (exact in bf16). The fast exp / sigmoid / rsqrt paths must
+    stay finite and match the oracle within the usual bars."""
+    import dataclasses
+    from gpu_cases import run_gpu
+    if variant == "saturated":
+        case = make_case(R=12, L=4, H=4, num_slots=64, seed=950, verify=True, beta_std=4.0,
+                         a_log_range=(2.0, 4.0))
+    else:
+        base = make_case(R=12, L=8, H=4, num_slots=128, seed=951, verify=True, beta_std=4.0,
+                         a_log_range=(-3.0, 4.0))
+        case = dataclasses.replace(base, projected=(base.projected.float() * 4.0).to(torch.bfloat16),
+                                   gate_lower_bound=-30.0)
+    before = case.state.numpy().copy()
+    ref = run_oracle(case)
+    got = run_gpu(case)
+    assert np.all(np.isfinite(got["state"])), "non-finite state"
+    assert_parity(case, ref, got, before, label=f"extreme: {variant}")
