@@ -30,11 +30,13 @@
  *
  * Conventions for every entry point:
  *   - Pointers marked "device" are HIP device pointers on the device that is
- *     current when kda_prepare runs; every later call must use that device.
+ *     current when kda_prepare runs; every later call on the handle must be
+ *     made with that device current (else KDA_ERR_DEVICE).
  *   - Sizes and strides are in elements unless a name says bytes.
  *   - Calls are asynchronous and stream ordered: they enqueue work on
  *     `hip_stream` (a hipStream_t, NULL = the null stream) and return.
- *   - Every argument is validated on the host before any HIP call. On a
+ *   - Every argument is validated on the host before anything is enqueued
+ *     (the only HIP call before that asks which device is current). On a
  *     non-KDA_OK status nothing was enqueued and no device memory changed,
  *     except for KDA_ERR_HIP (a HIP call failed; see kda_last_hip_error).
  *   - Nothing unwinds across the ABI; no function allocates on the host per
@@ -63,7 +65,8 @@ typedef enum {
     KDA_ERR_ALIGN = -3,       /* a pointer, pitch or stride breaks the alignment rules */
     KDA_ERR_UNSUPPORTED = -4, /* valid but not supported: conv width != 4, L > 8 */
     KDA_ERR_HIP = -5,         /* a HIP runtime call failed (kda_last_hip_error names it) */
-    KDA_ERR_NOMEM = -6        /* device or host allocation failed in kda_prepare */
+    KDA_ERR_NOMEM = -6,       /* device or host allocation failed in kda_prepare */
+    KDA_ERR_DEVICE = -7       /* the current HIP device is not the one the handle was prepared on */
 } kda_status;
 
 typedef struct kda_handle_s* kda_handle;
@@ -167,7 +170,8 @@ kda_status kda_prepare(const kda_weights* w, const kda_caches* c, void* hip_stre
  * read, no write, its core_out row untouched) and counted in the device error
  * counter (kda_device_errors). batch == 0 is a no-op.
  * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE (batch < 0, pitch too small or odd),
- * KDA_ERR_ALIGN, KDA_ERR_HIP. */
+ * KDA_ERR_ALIGN, KDA_ERR_DEVICE (called with another device current than the
+ * one kda_prepare ran on), KDA_ERR_HIP. */
 kda_status kda_decode(kda_handle h, const void* projected, int64_t pitch, int32_t batch,
                       const int32_t* slots, void* core_out, void* hip_stream);
 
@@ -226,10 +230,11 @@ kda_status kda_o_proj(const void* core, int64_t core_pitch, const void* w_o, voi
 
 /* Number of requests skipped for an out-of-range slot or accepted count since
  * the last read. Waits for `hip_stream`, copies the counter to *count_out and
- * resets it to zero. Errors: KDA_ERR_NULL, KDA_ERR_HIP. */
+ * resets it to zero. Errors: KDA_ERR_NULL, KDA_ERR_DEVICE, KDA_ERR_HIP. */
 kda_status kda_device_errors(kda_handle h, int32_t* count_out, void* hip_stream);
 
-/* Frees the handle and its device memory (after waiting for the device).
+/* Frees the handle and its device memory, after waiting for the handle's
+ * device (made current for the call; the caller's current device is restored).
  * NULL is a no-op. The borrowed caches are not touched. */
 kda_status kda_destroy(kda_handle h);
 

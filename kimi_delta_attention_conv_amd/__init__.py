@@ -30,7 +30,7 @@ ROUNDING = {"fused": 0, "bf16_handoff": 1}
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
 STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_ALIGN",
-          -4: "KDA_ERR_UNSUPPORTED", -5: "KDA_ERR_HIP", -6: "KDA_ERR_NOMEM"}
+          -4: "KDA_ERR_UNSUPPORTED", -5: "KDA_ERR_HIP", -6: "KDA_ERR_NOMEM", -7: "KDA_ERR_DEVICE"}
 
 
 class KdaError(RuntimeError):

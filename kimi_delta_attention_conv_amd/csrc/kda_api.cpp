@@ -1,6 +1,6 @@
 // Host side of the C ABI declared in include/kda.h: argument validation (all
-// of it before any HIP call), the handle and its device memory, and the
-// stream-ordered launches of the gfx950 kernels.
+// of it before anything is enqueued), the handle and its device memory, and
+// the stream-ordered launches of the gfx950 kernels.
 //
 // The call shapes follow page
 // "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.kda.prepared":
@@ -43,6 +43,14 @@ constexpr int64_t kAlign = 256;
 int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// The handle's pointers belong to the device kda_prepare ran on.
+kda_status check_device(const kda_handle_s* h) {
+    int d = -1;
+    hipError_t e = hipGetDevice(&d);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    return d == h->device ? KDA_OK : KDA_ERR_DEVICE;
+}
 
 kda_status check_call(const kda_handle_s* h, const void* projected, int64_t pitch,
                       int32_t requests, const int32_t* slots, const void* core_out) {
@@ -111,6 +119,7 @@ const char* kda_status_string(kda_status s) {
         case KDA_ERR_UNSUPPORTED: return "unsupported configuration (conv width must be 4, tokens <= 8)";
         case KDA_ERR_HIP: return "a HIP runtime call failed";
         case KDA_ERR_NOMEM: return "out of memory";
+        case KDA_ERR_DEVICE: return "the current device is not the handle's device";
     }
     return "unknown status";
 }
@@ -218,6 +227,7 @@ kda_status kda_decode(kda_handle h, const void* projected, int64_t pitch, int32_
                       const int32_t* slots, void* core_out, void* hip_stream) {
     kda_status st = check_call(h, projected, pitch, batch, slots, core_out);
     if (st != KDA_OK || batch == 0) return st;
+    if ((st = check_device(h)) != KDA_OK) return st;
     const kda::CoreParams p = core_params(h, projected, pitch, batch, slots, 1, nullptr, core_out);
     hipError_t e = kda::launch_core(1, p, static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? KDA_OK : hip_fail(e, "kda_decode launch");
@@ -235,6 +245,7 @@ kda_status kda_verify(kda_handle h, const void* projected, int64_t pitch, int32_
     if (accepted == nullptr) return KDA_ERR_NULL;
     if (!aligned(accepted, 4)) return KDA_ERR_ALIGN;
     if ((int64_t)requests * tokens > INT32_MAX) return KDA_ERR_SHAPE;
+    if ((st = check_device(h)) != KDA_OK) return st;
     const kda::CoreParams p =
         core_params(h, projected, pitch, requests, slots, slots_row_stride, accepted, core_out);
     hipError_t e = kda::launch_core(tokens, p, static_cast<hipStream_t>(hip_stream));
@@ -281,6 +292,8 @@ kda_status kda_o_proj(const void* core, int64_t core_pitch, const void* w_o, voi
 
 kda_status kda_device_errors(kda_handle h, int32_t* count_out, void* hip_stream) {
     if (h == nullptr || count_out == nullptr) return KDA_ERR_NULL;
+    const kda_status st = check_device(h);
+    if (st != KDA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     int32_t host = 0;
     hipError_t e = hipMemcpyAsync(&host, h->err_count, sizeof host, hipMemcpyDeviceToHost, s);
@@ -293,11 +306,17 @@ kda_status kda_device_errors(kda_handle h, int32_t* count_out, void* hip_stream)
 
 kda_status kda_destroy(kda_handle h) {
     if (h == nullptr) return KDA_OK;
+    int caller = -1;
+    hipError_t c = hipGetDevice(&caller);
+    if (c == hipSuccess && caller != h->device) c = hipSetDevice(h->device);
+    if (c != hipSuccess) return hip_fail(c, "kda_destroy device");   // handle kept: retry possible
     hipError_t e = hipDeviceSynchronize();
     hipError_t f = hipFree(h->dev_mem);
     delete h;
+    hipError_t r = caller != -1 ? hipSetDevice(caller) : hipSuccess;
     if (e != hipSuccess) return hip_fail(e, "kda_destroy sync");
     if (f != hipSuccess) return hip_fail(f, "kda_destroy free");
+    if (r != hipSuccess) return hip_fail(r, "kda_destroy restore device");
     return KDA_OK;
 }
 

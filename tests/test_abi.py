@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings(lib):
     seen = set()
-    for code in range(0, -7, -1):
+    for code in range(0, -8, -1):
         s = kda.kda_status_string(code)
         assert s and s not in seen
         seen.add(s)
