@@ -176,6 +176,9 @@ def linear(x, w, y=None, stream=None):
     M, N, K = x.shape[0], w.shape[0], w.shape[1]
     if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
         raise TypeError("x and w must be bfloat16")
+    if not (x.is_cuda and w.is_cuda and (y is None or y.is_cuda)) or w.device != x.device or \
+            (y is not None and y.device != x.device):
+        raise TypeError("x, w and y must be tensors on one GPU")
     if x.stride(1) != 1 or not w.is_contiguous() or x.shape[1] < K:
         raise ValueError("x needs unit column stride and >= K columns; w must be dense [N, K]")
     if y is None:
@@ -242,6 +245,11 @@ class KdaCore:
         if norm_weight.numel() not in (HEAD_DIM, D):
             raise ValueError("norm_weight must have 128 or H*128 elements")
         self.heads, self.dim = H, D
+        self.device = state.device
+        for name, t in (("conv_weight", conv_weight), ("f_b", f_b), ("A_log", A_log),
+                        ("dt_bias", dt_bias), ("norm_weight", norm_weight), ("conv", conv)):
+            if t.device != self.device:
+                raise TypeError(f"{name} is on {t.device}, the state pool on {self.device}")
         self.conv, self.state = conv, state
         w = KdaWeights(heads=H, conv_width=CONV_WIDTH, conv_weight=conv_weight.data_ptr(),
                        conv_bias=None if conv_bias is None else conv_bias.data_ptr(),
@@ -266,10 +274,18 @@ class KdaCore:
             return self._torch.cuda.current_stream().cuda_stream
         return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
+    def _on_device(self, **tensors):
+        for name, t in tensors.items():
+            if not t.is_cuda or t.device != self.device:
+                raise TypeError(f"{name} must be on {self.device} (the core's device)")
+
     def _rows(self, projected, out):
         torch = self._torch
         if projected.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
             raise TypeError("projected and out must be bfloat16")
+        self._on_device(projected=projected, out=out)
+        if projected.dim() == 2 and projected.shape[1] < 4 * self.dim + FA_RANK + self.heads:
+            raise ValueError("projected rows hold fewer than 4D + 128 + H columns")
         if projected.dim() != 2 or projected.stride(1) != 1 or out.dim() != 2 or \
                 out.stride(1) != 1 or out.shape[1] != self.dim or out.stride(0) != self.dim:
             raise ValueError("projected [S, pitch] and out [S, D] must be row-major")
@@ -280,6 +296,7 @@ class KdaCore:
     def decode(self, projected, out, slots, stream=None):
         """projected bf16 [B, pitch], out bf16 [B, D], slots int32 [B] (in place)."""
         pitch = self._rows(projected, out)
+        self._on_device(slots=slots)
         if slots.dtype != self._torch.int32 or slots.dim() != 1 or slots.stride(0) != 1:
             raise ValueError("slots must be a dense int32 [B] tensor")
         B = projected.shape[0]
@@ -294,6 +311,7 @@ class KdaCore:
         stride >= L, unit column stride), accepted int32 [>= R]."""
         pitch = self._rows(projected, out)
         torch = self._torch
+        self._on_device(slots=slots, accepted=accepted)
         if slots.dtype != torch.int32 or slots.dim() != 2 or slots.stride(1) != 1:
             raise ValueError("slots must be int32 [R, L] with unit column stride")
         if accepted.dtype != torch.int32 or accepted.dim() != 1 or accepted.stride(0) != 1:

@@ -189,6 +189,19 @@ def test_host_validation_leaves_device_untouched():
             with pytest.raises(kda.KdaError) as ei:
                 fn()
             assert ei.value.status == status
+        # the torch wrapper refuses host tensors and too-narrow rows before any call
+        core = g.core
+        p2d = p.view(case.S, case.pitch)
+        with pytest.raises(TypeError):
+            core.verify(p2d.cpu(), o, slots, acc)
+        with pytest.raises(TypeError):
+            core.verify(p2d, o, slots.cpu(), acc)
+        with pytest.raises(TypeError):
+            core.verify(p2d, o, slots, acc.cpu())
+        with pytest.raises(TypeError):
+            core.decode(p2d, o.cpu(), slots.reshape(-1))
+        with pytest.raises(ValueError):
+            core.verify(p2d[:, :case.pitch - 8], o, slots, acc)
         torch.cuda.synchronize()
         assert torch.equal(before, g.state)
         assert g.core.device_errors() == 0
