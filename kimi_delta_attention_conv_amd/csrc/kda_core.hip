@@ -102,13 +102,11 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
     const int wave = tid >> 6;
     const int lane = tid & 63;
 
-    __shared__ float s_qkv[L][3 * N];   // conv outputs; q, k normalised in place
+    __shared__ float s_qkv[L][3 * N];   // conv outputs q | k | v (raw: l2 scales applied later)
     __shared__ float s_eg[L][N];        // e^g per key channel
     __shared__ float s_gate[L][N];      // output gate (raw)
     __shared__ float s_o[L][N];         // recurrence outputs
     __shared__ float s_braw[L];
-    __shared__ float s_beta[L];
-    __shared__ float s_kq[L];           // k_hat . q_hat
     // conv windows after each token in the dim-first layout: channel cl's three
     // inputs at 3 cl .. 3 cl + 2 (the global order of one head's q, k, v runs)
     __shared__ __attribute__((aligned(16))) uint16_t s_win[L][3 * N * 3];
@@ -270,29 +268,12 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
     }
     __syncthreads();
 
-    // ---- l2norm of q and k, beta, k_hat . q_hat: wave t for token t
-    if (wave < L) {
-        const int t = wave;
-        float q0 = s_qkv[t][2 * lane], q1 = s_qkv[t][2 * lane + 1];
-        float k0 = s_qkv[t][N + 2 * lane], k1 = s_qkv[t][N + 2 * lane + 1];
-        const float sq = wave_sum(q0 * q0 + q1 * q1);
-        const float sk = wave_sum(k0 * k0 + k1 * k1);
-        const float qs = p.q_scale * __builtin_amdgcn_rsqf(sq + p.l2_eps);
-        const float ks = __builtin_amdgcn_rsqf(sk + p.l2_eps);
-        q0 *= qs; q1 *= qs; k0 *= ks; k1 *= ks;
-        s_qkv[t][2 * lane] = q0;
-        s_qkv[t][2 * lane + 1] = q1;
-        s_qkv[t][N + 2 * lane] = k0;
-        s_qkv[t][N + 2 * lane + 1] = k1;
-        const float kq = wave_sum(q0 * k0 + q1 * k1);
-        if (lane == 0) {
-            s_beta[t] = sigmoid(s_braw[t]);
-            s_kq[t] = kq;
-        }
-    }
-    __syncthreads();
-
-    // ---- the recurrence over the L tokens, a state stored per token
+    // ---- the recurrence over the L tokens, a state stored per token. Every
+    // wave takes the l2norm scales of q and k (and k . q) itself from the raw
+    // conv outputs: a lane's 16 columns, summed over the 8 lanes of a row, cover
+    // all 128 channels (the same reduction as the row dot products), so no
+    // second barrier is needed. With k_hat = ks k and q_hat = qs q:
+    //   (S k_hat) = ks (S k), (S q_hat) = qs (S q), k_hat . q_hat = ks qs (k . q).
 #pragma unroll
     for (int t = 0; t < L; ++t) {
         f32x4 eg[4], kk[4], qq[4];
@@ -302,8 +283,17 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
             qq[m] = *reinterpret_cast<const f32x4*>(&s_qkv[t][32 * m + csub]);
             kk[m] = *reinterpret_cast<const f32x4*>(&s_qkv[t][N + 32 * m + csub]);
         }
-        const float beta = s_beta[t];
-        const float kq = s_kq[t];
+        float sq = 0.0f, sk = 0.0f, skq = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            sq = dot4(qq[m], qq[m], sq);
+            sk = dot4(kk[m], kk[m], sk);
+            skq = dot4(kk[m], qq[m], skq);
+        }
+        const float qs = p.q_scale * __builtin_amdgcn_rsqf(sum8(sq) + p.l2_eps);
+        const float ks = __builtin_amdgcn_rsqf(sum8(sk) + p.l2_eps);
+        const float kq = qs * ks * sum8(skq);     // k_hat . q_hat
+        const float beta = sigmoid(s_braw[t]);
         float* dp = p.state + (int64_t)dst[t] * p.state_slot_stride + unit_off;
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
@@ -315,14 +305,15 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
                 a = dot4(S[g][m], kk[m], a);      // (S k)_row, decayed state
                 b = dot4(S[g][m], qq[m], b);      // (S q)_row, decayed state
             }
-            a = sum8(a);
-            b = sum8(b);
+            a = ks * sum8(a);                     // (S k_hat)_row
+            b = qs * sum8(b);                     // (S q_hat)_row
             const float bu = beta * (s_qkv[t][2 * N + row] - a);
-            // o = (S_decayed + bu k^T) q = b + bu (k . q)
+            // o = (S_decayed + bu k_hat^T) q_hat = b + bu (k_hat . q_hat)
             const float o = __builtin_fmaf(bu, kq, b);
+            const float buk = bu * ks;            // rank-1 update along k_hat = ks k
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                S[g][m] += bu * kk[m];
+                S[g][m] += buk * kk[m];
                 __builtin_nontemporal_store(S[g][m],
                                             reinterpret_cast<f32x4*>(dp + g * 8 * N + 32 * m));
             }
