@@ -11,8 +11,8 @@
 //
 // Three kernels, chosen by the row count M and K:
 //
-// Skinny (M <= 16, and up to 64 rows when K is not a multiple of 64): both
-// operands are K-contiguous (rows of X, rows of the nn.Linear weight W), so
+// Skinny (M <= 16 when K is a multiple of 64 but not of 128, up to 64 rows
+// when K is not a multiple of 64): both operands are K-contiguous (rows of X, rows of the nn.Linear weight W), so
 // every lane reads 64 contiguous bytes of one row per 128-wide K block and
 // feeds v_mfma_f32_16x16x32_bf16 directly from registers. Within a K block,
 // lane group kg (= lane >> 4) hands K elements 8 (kg + 4q) .. +8 to MFMA K
@@ -21,9 +21,9 @@
 // the K blocks round-robin and their partial tiles are summed through LDS in
 // wave order (a fixed order: results do not depend on timing).
 //
-// Direct-to-LDS (M > 16, K a multiple of 64): BM x BN tiles, X and W blocks
-// loaded straight into a ring of LDS stages. Tiled (M > 64, other K): 128 x 64
-// tiles staged through registers.
+// Direct-to-LDS (K a multiple of 128, or K a multiple of 64 and M > 16): BM x
+// BN tiles, X and W blocks loaded straight into a ring of LDS stages. Tiled
+// (M > 64, other K): 128 x 64 tiles staged through registers.
 #include "kda_internal.h"
 
 namespace kda {
@@ -279,7 +279,11 @@ __global__ __launch_bounds__(256) void linear_tiled_kernel(const LinearParams p)
 // With KS = 2 the waves form two groups that take the two 32-wide halves of
 // every K block (each wave's fragment reads per block halve while its tile
 // stays large); the groups' partial tiles are summed through LDS at the end.
-template <int BM, int BN, int STAGES, int WGM, int WGN, int KS>
+//
+// A stage holds SUB consecutive 64-wide K blocks (each in the layout above),
+// so one wait and one barrier cover SUB blocks and each row is fetched in
+// SUB x 128-byte runs.
+template <int BM, int BN, int STAGES, int WGM, int WGN, int KS, int SUB>
 __global__ __launch_bounds__(64 * WGM * WGN * KS) void linear_lds_kernel(const LinearParams p) {
     static_assert(KS == 1 || KS == 2, "K split of a 64-wide block into 1 or 2 parts");
     constexpr int WAVES = WGM * WGN * KS;
@@ -287,7 +291,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void linear_lds_kernel(const L
     constexpr int LPB = ROWS / (8 * WAVES);        // direct loads per thread per K block
     constexpr int TM = BM / WGM / 16, TN = BN / WGN / 16;   // 16 x 16 tiles per wave
     static_assert(LPB * 8 * WAVES == ROWS, "rows must split into whole wave loads");
-    __shared__ __attribute__((aligned(1024))) uint16_t sm[STAGES][ROWS * 64];
+    __shared__ __attribute__((aligned(1024))) uint16_t sm[STAGES][SUB][ROWS * 64];
 
     const int mblocks = (p.M + BM - 1) / BM;
     const int tiles = mblocks * ((p.N + BN - 1) / BN);
@@ -315,14 +319,17 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void linear_lds_kernel(const L
             ? p.X + (int64_t)min(m0 + row, p.M - 1) * p.x_pitch + 8 * chunk
             : p.W + (int64_t)min(n0 + row - BM, p.N - 1) * p.K + 8 * chunk;
     }
-    const int nkb = p.K / 64;
+    const int nkb = p.K / (64 * SUB);            // stages of K (the launch checks K % (64 SUB))
     auto issue = [&](int kb) {
         const int st = kb % STAGES;
-        const int kk = min(kb, nkb - 1) * 64;     // past the end: a harmless re-read
+        const int kk = min(kb, nkb - 1) * 64 * SUB;     // past the end: a harmless re-read
 #if defined(__HIP_DEVICE_COMPILE__)   // the builtin's LDS operand has no host type
 #pragma unroll
         for (int j = 0; j < LPB; ++j)
-            __builtin_amdgcn_global_load_lds(src[j] + kk, &sm[st][8 * (WAVES * j + wave) * 64], 16, 0, 0);
+#pragma unroll
+            for (int u = 0; u < SUB; ++u)
+                __builtin_amdgcn_global_load_lds(src[j] + kk + 64 * u, &sm[st][u][8 * (WAVES * j + wave) * 64],
+                                                 16, 0, 0);
 #endif
     };
 
@@ -335,15 +342,18 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void linear_lds_kernel(const L
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s) issue(s);
     for (int kb = 0; kb < nkb; ++kb) {
-        // block kb has landed once at most (STAGES - 2) blocks of loads are outstanding
-        constexpr int N = (STAGES - 2) * LPB;
+        // stage kb has landed once at most (STAGES - 2) stages of loads are outstanding
+        constexpr int N = (STAGES - 2) * LPB * SUB;
+        static_assert(N < 64, "the vmcnt field holds 6 bits");
         __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
         // a plain barrier: a fenced one would also wait for the direct loads still
         // in flight for later blocks; the memory clobber keeps LDS reads and new
         // direct loads on their side of it
         __asm__ volatile("s_barrier" ::: "memory");
         issue(kb + STAGES - 1);                   // into the stage read one block ago
-        const uint16_t* st = sm[kb % STAGES];
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) {
+        const uint16_t* st = sm[kb % STAGES][u];
 #pragma unroll
         for (int s = kh * (2 / KS); s < (kh + 1) * (2 / KS); ++s) {
             bf16x8 a[TM], b[TN];
@@ -365,12 +375,13 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void linear_lds_kernel(const L
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
+        }
     }
     __builtin_amdgcn_s_waitcnt(0);   // no direct load may still target LDS at exit
 
     if (KS == 2) {   // group 1 parks its tiles in the (now idle) stages, group 0 adds them
         static_assert(KS == 1 || WGM * WGN * TM * TN * 256 * 4 <= (int)sizeof(sm), "room to reduce");
-        float* red = reinterpret_cast<float*>(&sm[0][0]);
+        float* red = reinterpret_cast<float*>(&sm[0][0][0]);
         __syncthreads();
         if (kh == 1) {
 #pragma unroll
@@ -405,10 +416,11 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void linear_lds_kernel(const L
         }
 }
 
-template <int BM, int BN, int STAGES, int WGM, int WGN, int KS>
+template <int BM, int BN, int STAGES, int WGM, int WGN, int KS, int SUB = 1>
 hipError_t launch_lds(const LinearParams& p, hipStream_t s) {
+    if (p.K % (64 * SUB) != 0) return hipErrorInvalidValue;
     const int64_t tiles = (int64_t)((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
-    hipLaunchKernelGGL((linear_lds_kernel<BM, BN, STAGES, WGM, WGN, KS>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((linear_lds_kernel<BM, BN, STAGES, WGM, WGN, KS, SUB>), dim3((unsigned)tiles),
                        dim3(64 * WGM * WGN * KS), 0, s, p);
     return hipGetLastError();
 }
@@ -431,20 +443,28 @@ hipError_t launch_tiled(const LinearParams& p, hipStream_t s) {
 
 hipError_t launch_linear(const LinearParams& p, hipStream_t s) {
     // shapes measured on MI355X at the projections' sizes (7168 -> 6284,
-    // 1536 -> 7168). Up to 16 rows the skinny kernel (2 column tiles a wave, 8
-    // waves). Above that the direct-to-LDS kernel: 32 x 32 tiles with 8 stages
-    // up to 32 rows and 32 x 64 tiles with 6 stages up to 64 (two waves, or two
-    // pairs, on the two K halves of each block); 128 x 64 tiles of 4 x 2 waves
-    // with 4 stages up to 256 rows; 128 x 128 tiles of 2 x 4 waves per K half
-    // (16 waves) with 3 stages beyond. K not a multiple of 64 takes the skinny
-    // kernel up to 64 rows and the register-staged kernel above.
-    if (p.M <= 16) return launch_skinny<1, 2, 8>(p, s);
+    // 1536 -> 7168). With K a multiple of 128 and up to 64 rows, the
+    // direct-to-LDS kernel with two 64-wide K blocks a stage: 16 x 32 tiles
+    // (6 stages) up to 16 rows, 32 x 32 up to 32 and 32 x 64 up to 64 (4
+    // stages), one wave or wave pair on each 32-wide K half of a block. Above
+    // 64 rows (K a multiple of 64): 128 x 64 tiles of 4 x 2 waves with 4 stages
+    // up to 256 rows; 128 x 128 tiles of 2 x 4 waves per K half (16 waves) with
+    // 3 stages beyond. K a multiple of 64 only: one K block a stage up to 64
+    // rows (the skinny kernel up to 16). Other K: the skinny kernel up to 64
+    // rows and the register-staged kernel above.
+    if (p.K % 128 == 0 && p.M <= 64) {
+        if (p.M <= 16) return launch_lds<16, 32, 6, 1, 1, 2, 2>(p, s);
+        if (p.M <= 32) return launch_lds<32, 32, 4, 1, 1, 2, 2>(p, s);
+        return launch_lds<32, 64, 4, 1, 2, 2, 2>(p, s);
+    }
     if (p.K % 64 == 0) {
+        if (p.M <= 16) return launch_skinny<1, 2, 8>(p, s);
         if (p.M <= 32) return launch_lds<32, 32, 8, 1, 1, 2>(p, s);
         if (p.M <= 64) return launch_lds<32, 64, 6, 1, 2, 2>(p, s);
         if (p.M <= 256) return launch_lds<128, 64, 4, 4, 2, 1>(p, s);
         return launch_lds<128, 128, 3, 2, 4, 2>(p, s);
     }
+    if (p.M <= 16) return launch_skinny<1, 2, 8>(p, s);
     if (p.M <= 32) return launch_skinny<2, 2, 8>(p, s);
     if (p.M <= 64) return launch_skinny<4, 2, 8>(p, s);
     return launch_tiled<128, 64, 2>(p, s);

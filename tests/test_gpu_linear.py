@@ -78,7 +78,9 @@ def _check(x, w, got, ms=None, ns=None, label=""):
 @pytest.mark.parametrize("M,N,K", [(1, 1, 8), (5, 37, 136), (16, 16, 128), (17, 33, 264),
                                    (33, 100, 1024), (64, 48, 520), (70, 129, 384),
                                    (100, 77, 520), (256, 65, 64), (257, 130, 192),
-                                   (300, 200, 256), (20, 45, 128), (40, 65, 192), (17, 31, 64)])
+                                   (300, 200, 256), (20, 45, 128), (40, 65, 192), (17, 31, 64),
+                                   (9, 40, 192), (7, 70, 1152), (24, 97, 896), (1, 300, 256),
+                                   (64, 200, 1280)])
 def test_ragged_shapes(M, N, K):
     x, w = make_linear(M, N, K, seed=M * 1000 + N + K, x_pitch=K + 8)
     got = _run(x, w, y_pitch=N + 3)
@@ -86,7 +88,7 @@ def test_ragged_shapes(M, N, K):
     assert np.all(got[:, N:] == SENT), "columns beyond N were written"
 
 
-@pytest.mark.parametrize("rows", [64, 256, 512])
+@pytest.mark.parametrize("rows", [1, 16, 32, 64, 256, 512])
 def test_in_proj_full_shape(rows):
     heads = 12
     N = 4 * 128 * heads + 128 + heads
@@ -99,7 +101,7 @@ def test_in_proj_full_shape(rows):
     assert np.array_equal(got, again), "not deterministic"
 
 
-@pytest.mark.parametrize("rows", [64, 256, 512])
+@pytest.mark.parametrize("rows", [1, 16, 32, 64, 256, 512])
 def test_o_proj_full_shape(rows):
     heads = 12
     x, w = make_linear(rows, HIDDEN, 128 * heads, seed=10 + rows)
