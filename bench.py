@@ -152,10 +152,12 @@ def bench_projections(args, torch, kda):
         xs = x.cuda()
         ws = [w.cuda() for _ in range(copies)]
         y = torch.empty(S, N, dtype=torch.bfloat16, device="cuda")
+        ws_bytes = int(lib.kda_linear_workspace_bytes(S, N, K))
+        work = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
 
         def launch(i):
             return lib.kda_linear(xs.data_ptr(), xs.stride(0), ws[i % copies].data_ptr(),
-                                  y.data_ptr(), N, S, N, K, sp)
+                                  y.data_ptr(), N, S, N, K, work.data_ptr(), ws_bytes, sp)
         for i in range(args.warmup):
             assert launch(i) == 0
         torch.cuda.synchronize()
@@ -172,14 +174,14 @@ def bench_projections(args, torch, kda):
         gbps = nbytes / (ms * 1e-3) / 1e9
         t_mfma, t_hbm = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12), nbytes / (HBM_PEAK_GBPS * 1e9)
         bound = "mfma" if t_mfma >= t_hbm else "hbm"
-        out[name] = {"M": S, "N": N, "K": K, "us": round(ms * 1e3, 2),
+        out[name] = {"M": S, "N": N, "K": K, "split_k": ws_bytes > 0, "us": round(ms * 1e3, 2),
                      "tflops": round(tflops, 1), "gbps": round(gbps, 1),
                      "roofline": {"bound": bound,
                                   "achieved": round(tflops if bound == "mfma" else gbps, 1),
                                   "peak": MFMA_BF16_PEAK_TFLOPS if bound == "mfma" else HBM_PEAK_GBPS,
                                   "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
                                   "frac": round((t_mfma if bound == "mfma" else t_hbm) / (ms * 1e-3), 4)}}
-        del ws, xs, y
+        del ws, xs, y, work
         torch.cuda.empty_cache()
     return out
 
@@ -216,18 +218,22 @@ def bench_layer(args, torch, kda):
     sets = [torch.as_strided(slot_base, sh, st, off) for sh, st, off in views]
     accepted = None if case.accepted is None else case.accepted.to(dev)
     h = core.handle
+    # one workspace serves both projections (they run in stream order)
+    ws_bytes = max(int(lib.kda_linear_workspace_bytes(S, n_in, HIDDEN)),
+                   int(lib.kda_linear_workspace_bytes(S, HIDDEN, D)))
+    work = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     def parts(i, sp):
         w1, w2, sl = w_ins[i % copies], w_os[i % copies], sets[i % len(sets)]
         return [
             lambda: lib.kda_in_proj(xs.data_ptr(), HIDDEN, w1.data_ptr(), projected.data_ptr(),
-                                    pitch, S, HIDDEN, H, sp),
+                                    pitch, S, HIDDEN, H, work.data_ptr(), ws_bytes, sp),
             (lambda: lib.kda_decode(h, projected.data_ptr(), pitch, case.R, sl.data_ptr(),
                                     core_out.data_ptr(), sp)) if accepted is None else
             (lambda: lib.kda_verify(h, projected.data_ptr(), pitch, case.R, case.L, sl.data_ptr(),
                                     sl.stride(0), accepted.data_ptr(), core_out.data_ptr(), sp)),
             lambda: lib.kda_o_proj(core_out.data_ptr(), D, w2.data_ptr(), out.data_ptr(), HIDDEN,
-                                   S, H, HIDDEN, sp),
+                                   S, H, HIDDEN, work.data_ptr(), ws_bytes, sp),
         ]
 
     stream = torch.cuda.current_stream()
@@ -415,6 +421,10 @@ def main():
     sets = [torch.as_strided(slot_base, shape, stride, off) for shape, stride, off in views]
     accepted = None if case.accepted is None else case.accepted.to(dev)
     h = core.handle
+    # one workspace serves both projections (they run in stream order)
+    ws_bytes = max(int(lib.kda_linear_workspace_bytes(S, n_in, HIDDEN)),
+                   int(lib.kda_linear_workspace_bytes(S, HIDDEN, D)))
+    work = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     pitch = case.pitch
     lib = kda.load_library()
 

@@ -47,6 +47,7 @@
 #ifndef KDA_H
 #define KDA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -210,23 +211,41 @@ kda_status kda_verify(kda_handle h, const void* projected, int64_t pitch, int32_
  * aligned, K a multiple of 8; y rows y_pitch >= N elements apart, 2-byte
  * aligned; only columns 0 .. N-1 of each y row are written. All pointers are
  * device pointers borrowed for the call; the call is asynchronous on
- * hip_stream. The result is deterministic (a fixed summation order).
+ * hip_stream.
+ * Workspace: optional device memory (16-byte aligned) of workspace_bytes
+ * bytes. For the shapes kda_linear_workspace_bytes answers non-zero (33 to 64
+ * rows, K >= 4096 and a multiple of 256), a workspace of at least that size
+ * lets the call split K over 4 slices of workgroups: fp32 partial tiles go to
+ * the workspace and a second kernel on the same stream adds them in slice
+ * order. Its contents are undefined before and after the call; it must not be
+ * in use by another call still in flight (stream order is enough). NULL, or
+ * too small a size, runs the unsplit kernel.
+ * The result is deterministic for a given shape and choice of path (each
+ * path sums in a fixed order; the two paths may differ in the last bit).
  * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE (M < 0, N < 1, K < 8, K not a multiple
- * of 8, a pitch too small), KDA_ERR_ALIGN, KDA_ERR_HIP. M == 0 is a no-op. */
+ * of 8, a pitch too small), KDA_ERR_ALIGN (also a misaligned workspace),
+ * KDA_ERR_HIP. M == 0 is a no-op. */
 kda_status kda_linear(const void* x, int64_t x_pitch, const void* w, void* y, int64_t y_pitch,
-                      int32_t M, int32_t N, int32_t K, void* hip_stream);
+                      int32_t M, int32_t N, int32_t K, void* workspace, size_t workspace_bytes,
+                      void* hip_stream);
+
+/* Bytes of workspace with which kda_linear splits K for this shape; 0 when
+ * the shape is never split (or the shape is invalid). Host-only. */
+size_t kda_linear_workspace_bytes(int32_t M, int32_t N, int32_t K);
 
 /* in_proj: N = 4D + 128 + H packed outputs (D = 128 heads), K = hidden;
- * projected rows are `pitch` elements apart (pitch >= N). */
+ * projected rows are `pitch` elements apart (pitch >= N). Workspace as for
+ * kda_linear with that N and K. */
 kda_status kda_in_proj(const void* x, int64_t x_pitch, const void* w_in, void* projected,
                        int64_t pitch, int32_t rows, int32_t hidden, int32_t heads,
-                       void* hip_stream);
+                       void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* o_proj: N = hidden, K = D = 128 heads; core rows `core_pitch` elements
- * apart (core_pitch >= D, a multiple of 8), out rows `out_pitch` apart. */
+ * apart (core_pitch >= D, a multiple of 8), out rows `out_pitch` apart.
+ * Workspace as for kda_linear with that N and K. */
 kda_status kda_o_proj(const void* core, int64_t core_pitch, const void* w_o, void* out,
                       int64_t out_pitch, int32_t rows, int32_t heads, int32_t hidden,
-                      void* hip_stream);
+                      void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Number of requests skipped for an out-of-range slot or accepted count since
  * the last read. Waits for `hip_stream`, copies the counter to *count_out and

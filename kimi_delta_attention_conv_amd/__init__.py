@@ -16,7 +16,7 @@ import os
 __all__ = [
     "KdaError", "KdaWeights", "KdaCaches", "load_library", "kda_prepare", "kda_decode",
     "kda_verify", "kda_device_errors", "kda_destroy", "kda_status_string", "KdaCore",
-    "kda_linear", "kda_in_proj", "kda_o_proj", "linear",
+    "kda_linear", "kda_linear_workspace_bytes", "kda_in_proj", "kda_o_proj", "linear",
     "HEAD_DIM", "FA_RANK", "CONV_WIDTH", "MAX_TOKENS", "ROUNDING",
 ]
 
@@ -92,11 +92,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_hip_error.argtypes = []
     lib.kda_last_hip_error.restype = ctypes.c_char_p
-    lib.kda_linear.argtypes = [vp, i64, vp, vp, i64, i32, i32, i32, vp]
-    lib.kda_in_proj.argtypes = [vp, i64, vp, vp, i64, i32, i32, i32, vp]
-    lib.kda_o_proj.argtypes = [vp, i64, vp, vp, i64, i32, i32, i32, vp]
+    sz = ctypes.c_size_t
+    lib.kda_linear.argtypes = [vp, i64, vp, vp, i64, i32, i32, i32, vp, sz, vp]
+    lib.kda_in_proj.argtypes = [vp, i64, vp, vp, i64, i32, i32, i32, vp, sz, vp]
+    lib.kda_o_proj.argtypes = [vp, i64, vp, vp, i64, i32, i32, i32, vp, sz, vp]
     for f in (lib.kda_linear, lib.kda_in_proj, lib.kda_o_proj):
         f.restype = ctypes.c_int
+    lib.kda_linear_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.kda_linear_workspace_bytes.restype = sz
     # HBM stream probes (include/kda_probe.h), measurement only
     lib.kda_probe_copy.argtypes = [vp, vp, i64, vp]
     lib.kda_probe_write.argtypes = [vp, i64, ctypes.c_float, vp]
@@ -146,20 +149,27 @@ def kda_verify(handle: int, projected: int, pitch: int, requests: int, tokens: i
 
 
 def kda_linear(x: int, x_pitch: int, w: int, y: int, y_pitch: int, M: int, N: int, K: int,
-               stream: int = 0) -> None:
-    _check(load_library().kda_linear(x, x_pitch, w, y, y_pitch, M, N, K, stream), "kda_linear")
+               workspace: int = 0, workspace_bytes: int = 0, stream: int = 0) -> None:
+    _check(load_library().kda_linear(x, x_pitch, w, y, y_pitch, M, N, K, workspace,
+                                     workspace_bytes, stream), "kda_linear")
+
+
+def kda_linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(load_library().kda_linear_workspace_bytes(M, N, K))
 
 
 def kda_in_proj(x: int, x_pitch: int, w_in: int, projected: int, pitch: int, rows: int,
-                hidden: int, heads: int, stream: int = 0) -> None:
+                hidden: int, heads: int, workspace: int = 0, workspace_bytes: int = 0,
+                stream: int = 0) -> None:
     _check(load_library().kda_in_proj(x, x_pitch, w_in, projected, pitch, rows, hidden, heads,
-                                      stream), "kda_in_proj")
+                                      workspace, workspace_bytes, stream), "kda_in_proj")
 
 
 def kda_o_proj(core: int, core_pitch: int, w_o: int, out: int, out_pitch: int, rows: int,
-               heads: int, hidden: int, stream: int = 0) -> None:
+               heads: int, hidden: int, workspace: int = 0, workspace_bytes: int = 0,
+               stream: int = 0) -> None:
     _check(load_library().kda_o_proj(core, core_pitch, w_o, out, out_pitch, rows, heads, hidden,
-                                     stream), "kda_o_proj")
+                                     workspace, workspace_bytes, stream), "kda_o_proj")
 
 
 def _stream_of(stream):
@@ -169,9 +179,12 @@ def _stream_of(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def linear(x, w, y=None, stream=None):
+def linear(x, w, y=None, stream=None, workspace="auto"):
     """y = x w^T for bf16 device tensors x [M, >=K] (unit column stride), w [N, K]
-    (dense); y [M, >=N] is allocated when not given. Returns y."""
+    (dense); y [M, >=N] is allocated when not given. `workspace`: "auto"
+    allocates the split-K workspace kda_linear_workspace_bytes asks for (none for
+    shapes that do not split), None passes none (the unsplit kernel), a device
+    tensor is used as given. Returns y."""
     import torch
     M, N, K = x.shape[0], w.shape[0], w.shape[1]
     if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
@@ -185,8 +198,18 @@ def linear(x, w, y=None, stream=None):
         y = torch.empty(M, N, dtype=torch.bfloat16, device=x.device)
     if y.dtype != torch.bfloat16 or y.stride(1) != 1 or y.shape[0] < M or y.shape[1] < N:
         raise ValueError("y must be bfloat16 [>= M, >= N] with unit column stride")
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a device tensor')
+        nbytes = kda_linear_workspace_bytes(M, N, K) if M > 0 else 0
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
+    if workspace is not None and (not workspace.is_cuda or workspace.device != x.device or
+                                  not workspace.is_contiguous()):
+        raise TypeError("workspace must be a contiguous tensor on x's GPU")
+    ws_ptr = 0 if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     kda_linear(x.data_ptr(), x.stride(0), w.data_ptr(), y.data_ptr(), y.stride(0), M, N, K,
-               _stream_of(stream))
+               ws_ptr, ws_bytes, _stream_of(stream))
     return y
 
 

@@ -253,13 +253,15 @@ kda_status kda_verify(kda_handle h, const void* projected, int64_t pitch, int32_
 }
 
 kda_status kda_linear(const void* x, int64_t x_pitch, const void* w, void* y, int64_t y_pitch,
-                      int32_t M, int32_t N, int32_t K, void* hip_stream) {
+                      int32_t M, int32_t N, int32_t K, void* workspace, size_t workspace_bytes,
+                      void* hip_stream) {
     if (M < 0 || N < 1 || K < 8 || K % 8 != 0) return KDA_ERR_SHAPE;
     if (M > (1 << 20)) return KDA_ERR_SHAPE;   // grid y limit at 64 rows a workgroup
     if (M == 0) return KDA_OK;
     if (x == nullptr || w == nullptr || y == nullptr) return KDA_ERR_NULL;
     if (x_pitch < K || y_pitch < N) return KDA_ERR_SHAPE;
-    if (x_pitch % 8 != 0 || !aligned(x, 16) || !aligned(w, 16) || !aligned(y, 2))
+    if (x_pitch % 8 != 0 || !aligned(x, 16) || !aligned(w, 16) || !aligned(y, 2) ||
+        !aligned(workspace, 16))
         return KDA_ERR_ALIGN;
     kda::LinearParams p{};
     p.X = static_cast<const uint16_t*>(x);
@@ -270,24 +272,32 @@ kda_status kda_linear(const void* x, int64_t x_pitch, const void* w, void* y, in
     p.M = M;
     p.N = N;
     p.K = K;
+    p.part = static_cast<float*>(workspace);
+    p.part_floats = workspace == nullptr ? 0 : (int64_t)(workspace_bytes / sizeof(float));
     hipError_t e = kda::launch_linear(p, static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? KDA_OK : hip_fail(e, "kda_linear launch");
 }
 
+size_t kda_linear_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+    if (M < 1 || N < 1 || K < 8 || K % 8 != 0 || M > (1 << 20)) return 0;
+    return (size_t)kda::linear_workspace_floats(M, N, K) * sizeof(float);
+}
+
 kda_status kda_in_proj(const void* x, int64_t x_pitch, const void* w_in, void* projected,
                        int64_t pitch, int32_t rows, int32_t hidden, int32_t heads,
-                       void* hip_stream) {
+                       void* workspace, size_t workspace_bytes, void* hip_stream) {
     if (heads < 1 || heads > 4096) return KDA_ERR_SHAPE;
     const int32_t N = 4 * heads * kda::kHeadDim + kda::kFaRank + heads;
-    return kda_linear(x, x_pitch, w_in, projected, pitch, rows, N, hidden, hip_stream);
+    return kda_linear(x, x_pitch, w_in, projected, pitch, rows, N, hidden, workspace,
+                      workspace_bytes, hip_stream);
 }
 
 kda_status kda_o_proj(const void* core, int64_t core_pitch, const void* w_o, void* out,
                       int64_t out_pitch, int32_t rows, int32_t heads, int32_t hidden,
-                      void* hip_stream) {
+                      void* workspace, size_t workspace_bytes, void* hip_stream) {
     if (heads < 1 || heads > 4096) return KDA_ERR_SHAPE;
     return kda_linear(core, core_pitch, w_o, out, out_pitch, rows, hidden,
-                      heads * kda::kHeadDim, hip_stream);
+                      heads * kda::kHeadDim, workspace, workspace_bytes, hip_stream);
 }
 
 kda_status kda_device_errors(kda_handle h, int32_t* count_out, void* hip_stream) {

@@ -74,10 +74,14 @@ struct LinearParams {
     uint16_t* Y;         // rows y_pitch elements apart
     int64_t y_pitch;
     int32_t M, N, K;     // K a multiple of 8
+    float* part;         // fp32 workspace for a K split, or null
+    int64_t part_floats; // its capacity in floats
 };
 
 hipError_t launch_prepare(const PrepareParams& in, const PreparedWeights& out, hipStream_t s);
 hipError_t launch_linear(const LinearParams& p, hipStream_t s);
+// Workspace floats launch_linear uses for a K split of this shape (0: none).
+int64_t linear_workspace_floats(int32_t M, int32_t N, int32_t K);
 hipError_t launch_core(int tokens, const CoreParams& p, hipStream_t s);
 
 }  // namespace kda

@@ -283,7 +283,15 @@ __global__ __launch_bounds__(256) void linear_tiled_kernel(const LinearParams p)
 // A stage holds SUB consecutive 64-wide K blocks (each in the layout above),
 // so one wait and one barrier cover SUB blocks and each row is fetched in
 // SUB x 128-byte runs.
-template <int BM, int BN, int STAGES, int WGM, int WGN, int KS, int SUB>
+//
+// With SPLIT > 1 the K range is cut into SPLIT equal slices, one workgroup a
+// (tile, slice); each writes its fp32 tile to p.part in fragment order (every
+// lane's four accumulators as one 16-byte run, lanes contiguous) and
+// linear_split_sum adds the slices in slice order. The slices of a tile are
+// consecutive workgroups, so with the round-robin placement of workgroups on
+// the 8 XCDs (SPLIT dividing 8) each XCD works on one K slice and its L2 holds
+// that slice of X for all of its workgroups.
+template <int BM, int BN, int STAGES, int WGM, int WGN, int KS, int SUB, int SPLIT>
 __global__ __launch_bounds__(64 * WGM * WGN * KS) void linear_lds_kernel(const LinearParams p) {
     static_assert(KS == 1 || KS == 2, "K split of a 64-wide block into 1 or 2 parts");
     constexpr int WAVES = WGM * WGN * KS;
@@ -293,15 +301,20 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void linear_lds_kernel(const L
     static_assert(LPB * 8 * WAVES == ROWS, "rows must split into whole wave loads");
     __shared__ __attribute__((aligned(1024))) uint16_t sm[STAGES][SUB][ROWS * 64];
 
+    static_assert(SPLIT == 1 || 8 % SPLIT == 0, "K slices map onto the 8 XCDs");
     const int mblocks = (p.M + BM - 1) / BM;
     const int tiles = mblocks * ((p.N + BN - 1) / BN);
-    int t = blockIdx.x;
-    {
+    int t = blockIdx.x, slice = 0;
+    if (SPLIT > 1) {
+        slice = blockIdx.x % SPLIT;
+        t = blockIdx.x / SPLIT;
+    } else {
         const int q = tiles >> 3;
         if ((int)blockIdx.x < 8 * q) t = (blockIdx.x & 7) * q + (blockIdx.x >> 3);
     }
     const int m0 = (t % mblocks) * BM;
     const int n0 = (t / mblocks) * BN;
+    const int kc = p.K / SPLIT;                   // this workgroup's K slice
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int kh = wave / (WGM * WGN);            // K part of this wave's group
     const int slot = wave % (WGM * WGN);          // tile position within the group
@@ -315,11 +328,11 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void linear_lds_kernel(const L
     for (int j = 0; j < LPB; ++j) {
         const int row = 8 * (WAVES * j + wave) + (lane >> 3);
         const int chunk = (lane & 7) ^ (lane >> 3);
-        src[j] = row < BM
-            ? p.X + (int64_t)min(m0 + row, p.M - 1) * p.x_pitch + 8 * chunk
-            : p.W + (int64_t)min(n0 + row - BM, p.N - 1) * p.K + 8 * chunk;
+        src[j] = (row < BM
+            ? p.X + (int64_t)min(m0 + row, p.M - 1) * p.x_pitch
+            : p.W + (int64_t)min(n0 + row - BM, p.N - 1) * p.K) + slice * kc + 8 * chunk;
     }
-    const int nkb = p.K / (64 * SUB);            // stages of K (the launch checks K % (64 SUB))
+    const int nkb = kc / (64 * SUB);             // stages of K (the launch checks K % (64 SUB SPLIT))
     auto issue = [&](int kb) {
         const int st = kb % STAGES;
         const int kk = min(kb, nkb - 1) * 64 * SUB;     // past the end: a harmless re-read
@@ -403,6 +416,15 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void linear_lds_kernel(const L
                     acc[i][j][r] += red[((slot * TM + i) * TN + j) * 256 + r * 64 + lane];
     }
 
+    if (SPLIT > 1) {
+        f32x4* out = reinterpret_cast<f32x4*>(p.part) +
+                     (((int64_t)slice * tiles + t) * (WGM * WGN) + slot) * (TM * TN * 64);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) out[(i * TN + j) * 64 + lane] = acc[i][j];
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -416,12 +438,55 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void linear_lds_kernel(const L
         }
 }
 
-template <int BM, int BN, int STAGES, int WGM, int WGN, int KS, int SUB = 1>
+// Sum of the SPLIT fp32 slices of linear_lds_kernel's tiles, in slice order
+// (a fixed order), rounded to bf16. One thread per fragment (one lane's four
+// accumulators of one 16 x 16 tile): it reads that fragment's 16-byte run in
+// every slice and writes the four outputs it holds.
+template <int BM, int BN, int WGM, int WGN, int SPLIT>
+__global__ __launch_bounds__(256) void linear_split_sum(const LinearParams p) {
+    constexpr int TM = BM / WGM / 16, TN = BN / WGN / 16;
+    const int mblocks = (p.M + BM - 1) / BM;
+    const int64_t tiles = (int64_t)mblocks * ((p.N + BN - 1) / BN);
+    const int64_t frags = tiles * (BM * BN / 4);          // fragments in one slice
+    const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (f >= frags) return;
+    const f32x4* part = reinterpret_cast<const f32x4*>(p.part);
+    f32x4 sum = part[f];
+#pragma unroll
+    for (int k = 1; k < SPLIT; ++k) sum += part[k * frags + f];
+    const int lane = (int)(f & 63);
+    const int64_t q = f >> 6;                             // (tile, slot, i, j)
+    const int ij = (int)(q % (TM * TN));
+    const int slot = (int)((q / (TM * TN)) % (WGM * WGN));
+    const int t = (int)(q / (TM * TN * WGM * WGN));
+    const int i = ij / TN, j = ij % TN;
+    const int n = (t / mblocks) * BN + (slot % WGN) * (BN / WGN) + 16 * j + (lane & 15);
+    if (n >= p.N) return;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int m = (t % mblocks) * BM + (slot / WGN) * (BM / WGM) + 16 * i + 4 * (lane >> 4) + r;
+        if (m < p.M) p.Y[(int64_t)m * p.y_pitch + n] = to_bf16(sum[r]);
+    }
+}
+
+template <int BM, int BN>
+int64_t split_floats(const LinearParams& p, int split) {
+    return (int64_t)split * ((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM) * BM * BN;
+}
+
+template <int BM, int BN, int STAGES, int WGM, int WGN, int KS, int SUB = 1, int SPLIT = 1>
 hipError_t launch_lds(const LinearParams& p, hipStream_t s) {
-    if (p.K % (64 * SUB) != 0) return hipErrorInvalidValue;
+    if (p.K % (64 * SUB * SPLIT) != 0) return hipErrorInvalidValue;
+    if (SPLIT > 1 && (p.part == nullptr || p.part_floats < split_floats<BM, BN>(p, SPLIT)))
+        return hipErrorInvalidValue;
     const int64_t tiles = (int64_t)((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
-    hipLaunchKernelGGL((linear_lds_kernel<BM, BN, STAGES, WGM, WGN, KS, SUB>), dim3((unsigned)tiles),
-                       dim3(64 * WGM * WGN * KS), 0, s, p);
+    hipLaunchKernelGGL((linear_lds_kernel<BM, BN, STAGES, WGM, WGN, KS, SUB, SPLIT>),
+                       dim3((unsigned)(tiles * SPLIT)), dim3(64 * WGM * WGN * KS), 0, s, p);
+    if (SPLIT > 1) {
+        const int64_t frags = tiles * (BM * BN / 4);
+        hipLaunchKernelGGL((linear_split_sum<BM, BN, WGM, WGN, SPLIT>), dim3((unsigned)((frags + 255) / 256)),
+                           dim3(256), 0, s, p);
+    }
     return hipGetLastError();
 }
 
@@ -439,11 +504,31 @@ hipError_t launch_tiled(const LinearParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The K split: 33 to 64 rows with a long K. One 64 x 128 tile then covers
+// all rows (X is read once per 128 columns instead of once per 32 or 64) and
+// 4 K slices make ~200 workgroups for the W stream, at the cost of the fp32
+// slices and a second launch; with a short K (o_proj) that cost outweighs it.
+constexpr int kSplit = 4;
+bool split_shape(int32_t M, int32_t K) {
+    return M > 32 && M <= 64 && K >= 4096 && K % (64 * kSplit) == 0;
+}
+
 }  // namespace
+
+int64_t linear_workspace_floats(int32_t M, int32_t N, int32_t K) {
+    if (M < 1 || N < 1 || !split_shape(M, K)) return 0;
+    LinearParams p{};
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    return split_floats<64, 128>(p, kSplit);
+}
 
 hipError_t launch_linear(const LinearParams& p, hipStream_t s) {
     // shapes measured on MI355X at the projections' sizes (7168 -> 6284,
-    // 1536 -> 7168). With K a multiple of 128 and up to 64 rows, the
+    // 1536 -> 7168). With a workspace, 33 to 64 rows and K >= 4096: 64 x 128
+    // tiles of 2 x 2 waves per K half, 4 K slices. With K a multiple of 128
+    // and up to 64 rows, the
     // direct-to-LDS kernel with two 64-wide K blocks a stage: 16 x 32 tiles
     // (6 stages) up to 16 rows, 32 x 32 up to 32 and 32 x 64 up to 64 (4
     // stages), one wave or wave pair on each 32-wide K half of a block. Above
@@ -452,6 +537,9 @@ hipError_t launch_linear(const LinearParams& p, hipStream_t s) {
     // 3 stages beyond. K a multiple of 64 only: one K block a stage up to 64
     // rows (the skinny kernel up to 16). Other K: the skinny kernel up to 64
     // rows and the register-staged kernel above.
+    if (split_shape(p.M, p.K) && p.part != nullptr &&
+        p.part_floats >= linear_workspace_floats(p.M, p.N, p.K))
+        return launch_lds<64, 128, 4, 2, 2, 2, 1, kSplit>(p, s);
     if (p.K % 128 == 0 && p.M <= 64) {
         if (p.M <= 16) return launch_lds<16, 32, 6, 1, 1, 2, 2>(p, s);
         if (p.M <= 32) return launch_lds<32, 32, 4, 1, 1, 2, 2>(p, s);

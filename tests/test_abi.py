@@ -113,6 +113,15 @@ def test_probe_validation_without_gpu(lib):
     assert lib.kda_probe_sink_floats() > 0
 
 
+def test_linear_workspace_bytes(lib):
+    # 33..64 rows, K >= 4096 and a multiple of 256: 4 K slices of 64 x 128 fp32 tiles
+    assert lib.kda_linear_workspace_bytes(64, 6284, 7168) == 4 * 50 * 64 * 128 * 4
+    assert lib.kda_linear_workspace_bytes(33, 128, 4096) == 4 * 64 * 128 * 4
+    for M, N, K in [(32, 6284, 7168), (65, 6284, 7168), (64, 7168, 1536), (64, 100, 4160),
+                    (0, 10, 4096), (64, 0, 4096), (64, 10, 4100)]:
+        assert lib.kda_linear_workspace_bytes(M, N, K) == 0, (M, N, K)
+
+
 def test_calls_on_null_handle(lib):
     n = ctypes.c_int32(7)
     assert lib.kda_decode(None, 0x1000, 1154, 1, 0x2000, 0x3000, None) == -1

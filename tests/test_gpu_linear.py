@@ -30,7 +30,9 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-def _run(x, w, y_pitch=None, M=None, fn="linear", heads=None):
+def _run(x, w, y_pitch=None, M=None, fn="linear", heads=None, workspace=None):
+    """workspace: None (no workspace: the unsplit kernel), "auto" (the size the
+    library asks for), or a byte count."""
     import kimi_delta_attention_conv_amd as kda
     M = x.shape[0] if M is None else M
     N, K = w.shape
@@ -38,14 +40,19 @@ def _run(x, w, y_pitch=None, M=None, fn="linear", heads=None):
     xd, wd = x.cuda(), w.cuda()
     y = torch.full((max(M, 1), y_pitch), SENT, dtype=torch.int16).view(torch.bfloat16).cuda()
     s = torch.cuda.current_stream().cuda_stream
+    nbytes = kda.kda_linear_workspace_bytes(M, N, K) if workspace == "auto" else (workspace or 0)
+    # the workspace starts as NaN patterns: no result may depend on its contents
+    work = torch.full((max(nbytes, 16) // 2,), SENT, dtype=torch.int16, device="cuda")
+    wp = work.data_ptr() if workspace is not None else 0
     if fn == "linear":
-        kda.kda_linear(xd.data_ptr(), xd.stride(0), wd.data_ptr(), y.data_ptr(), y_pitch, M, N, K, s)
+        kda.kda_linear(xd.data_ptr(), xd.stride(0), wd.data_ptr(), y.data_ptr(), y_pitch, M, N, K,
+                       wp, nbytes, stream=s)
     elif fn == "in_proj":
         kda.kda_in_proj(xd.data_ptr(), xd.stride(0), wd.data_ptr(), y.data_ptr(), y_pitch, M, K,
-                        heads, s)
+                        heads, wp, nbytes, stream=s)
     else:
         kda.kda_o_proj(xd.data_ptr(), xd.stride(0), wd.data_ptr(), y.data_ptr(), y_pitch, M,
-                       heads, N, s)
+                       heads, N, wp, nbytes, stream=s)
     torch.cuda.synchronize()
     return bf16_np(y.cpu())
 
@@ -101,6 +108,41 @@ def test_in_proj_full_shape(rows):
     assert np.array_equal(got, again), "not deterministic"
 
 
+@pytest.mark.parametrize("rows", [33, 48, 64])
+def test_in_proj_split_k(rows):
+    """33 to 64 rows with a workspace: K split over 4 slices, then the ordered sum."""
+    import kimi_delta_attention_conv_amd as kda
+    heads = 12
+    N = 4 * 128 * heads + 128 + heads
+    assert kda.kda_linear_workspace_bytes(rows, N, HIDDEN) > 0
+    x, w = make_linear(rows, N, HIDDEN, seed=300 + rows)
+    got = _run(x, w, y_pitch=N + 5, fn="in_proj", heads=heads, workspace="auto")
+    assert np.all(got[:, N:] == SENT), "columns beyond N were written"
+    got = got[:, :N]
+    rng = np.random.default_rng(rows + 7)
+    ms, ns = rng.integers(0, rows, 4000), rng.integers(0, N, 4000)
+    ms[:2], ns[:2] = rows - 1, N - 1           # the last row and column of the last tile
+    _check(x, w, got, ms, ns, label=f"in_proj split rows={rows}")
+    again = _run(x, w, fn="in_proj", heads=heads, workspace="auto")
+    assert np.array_equal(got, again), "not deterministic"
+    # too small a workspace takes the unsplit kernel, as does none at all
+    small = _run(x, w, fn="in_proj", heads=heads,
+                 workspace=kda.kda_linear_workspace_bytes(rows, N, HIDDEN) - 16)
+    none = _run(x, w, fn="in_proj", heads=heads)
+    assert np.array_equal(small, none)
+    _check(x, w, none, ms, ns, label=f"in_proj unsplit rows={rows}")
+
+
+@pytest.mark.parametrize("M,N", [(40, 300), (64, 129), (33, 1)])
+def test_split_k_ragged_full(M, N):
+    """Every output of a split shape whose N is not a multiple of the 128-wide tile."""
+    K = 4096
+    x, w = make_linear(M, N, K, seed=M * 31 + N, x_pitch=K + 8)
+    got = _run(x, w, y_pitch=N + 3, workspace="auto")
+    _check(x, w, got[:, :N], label=f"split M={M} N={N} K={K}")
+    assert np.all(got[:, N:] == SENT), "columns beyond N were written"
+
+
 @pytest.mark.parametrize("rows", [1, 16, 32, 64, 256, 512])
 def test_o_proj_full_shape(rows):
     heads = 12
@@ -124,6 +166,10 @@ def test_validation():
         with pytest.raises(kda.KdaError) as ei:
             kda.kda_linear(*args)
         assert ei.value.status == status
+    with pytest.raises(kda.KdaError) as ei:   # a workspace not 16-byte aligned
+        kda.kda_linear(xd.data_ptr(), 64, wd.data_ptr(), y.data_ptr(), 16, 4, 16, 64,
+                       y.data_ptr() + 4, 64)
+    assert ei.value.status == -3
     kda.kda_linear(0, 64, 0, 0, 16, 0, 16, 64)   # M == 0: no-op
     torch.cuda.synchronize()
     assert torch.all(y == 0)
