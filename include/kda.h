@@ -213,7 +213,7 @@ kda_status kda_verify(kda_handle h, const void* projected, int64_t pitch, int32_
  * device pointers borrowed for the call; the call is asynchronous on
  * hip_stream.
  * Workspace: optional device memory (16-byte aligned) of workspace_bytes
- * bytes. For the shapes kda_linear_workspace_bytes answers non-zero (33 to 64
+ * bytes. For the shapes kda_linear_workspace_bytes answers non-zero (33 to 256
  * rows, K >= 4096 and a multiple of 256), a workspace of at least that size
  * lets the call split K over 4 slices of workgroups: fp32 partial tiles go to
  * the workspace and a second kernel on the same stream adds them in slice

@@ -504,13 +504,14 @@ hipError_t launch_tiled(const LinearParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-// The K split: 33 to 64 rows with a long K. One 64 x 128 tile then covers
-// all rows (X is read once per 128 columns instead of once per 32 or 64) and
-// 4 K slices make ~200 workgroups for the W stream, at the cost of the fp32
-// slices and a second launch; with a short K (o_proj) that cost outweighs it.
+// The K split, for 33 to 256 rows with a long K: one tile covers up to 64,
+// 128 or 256 rows x 128 columns (X is read once per 128 columns, W once per
+// tile) and 4 K slices make ~200 workgroups for the W stream, at the cost of
+// the fp32 slices and a second launch. With a short K (o_proj) or beyond 256
+// rows that cost outweighs the gain.
 constexpr int kSplit = 4;
 bool split_shape(int32_t M, int32_t K) {
-    return M > 32 && M <= 64 && K >= 4096 && K % (64 * kSplit) == 0;
+    return M > 32 && M <= 256 && K >= 4096 && K % (64 * kSplit) == 0;
 }
 
 }  // namespace
@@ -521,14 +522,17 @@ int64_t linear_workspace_floats(int32_t M, int32_t N, int32_t K) {
     p.M = M;
     p.N = N;
     p.K = K;
-    return split_floats<64, 128>(p, kSplit);
+    if (M <= 64) return split_floats<64, 128>(p, kSplit);
+    if (M <= 128) return split_floats<128, 128>(p, kSplit);
+    return split_floats<256, 128>(p, kSplit);
 }
 
 hipError_t launch_linear(const LinearParams& p, hipStream_t s) {
     // shapes measured on MI355X at the projections' sizes (7168 -> 6284,
-    // 1536 -> 7168). With a workspace, 33 to 64 rows and K >= 4096: 64 x 128
-    // tiles of 2 x 2 waves per K half, 4 K slices. With K a multiple of 128
-    // and up to 64 rows, the
+    // 1536 -> 7168). With a workspace, 33 to 256 rows and K >= 4096, 4 K
+    // slices of 64 x 128 tiles (2 x 2 waves per K half) up to 64 rows,
+    // 128 x 128 (2 x 4) up to 128 and 256 x 128 (4 x 2, 3 stages) up to 256.
+    // With K a multiple of 128 and up to 64 rows, the
     // direct-to-LDS kernel with two 64-wide K blocks a stage: 16 x 32 tiles
     // (6 stages) up to 16 rows, 32 x 32 up to 32 and 32 x 64 up to 64 (4
     // stages), one wave or wave pair on each 32-wide K half of a block. Above
@@ -538,8 +542,11 @@ hipError_t launch_linear(const LinearParams& p, hipStream_t s) {
     // rows (the skinny kernel up to 16). Other K: the skinny kernel up to 64
     // rows and the register-staged kernel above.
     if (split_shape(p.M, p.K) && p.part != nullptr &&
-        p.part_floats >= linear_workspace_floats(p.M, p.N, p.K))
-        return launch_lds<64, 128, 4, 2, 2, 2, 1, kSplit>(p, s);
+        p.part_floats >= linear_workspace_floats(p.M, p.N, p.K)) {
+        if (p.M <= 64) return launch_lds<64, 128, 4, 2, 2, 2, 1, kSplit>(p, s);
+        if (p.M <= 128) return launch_lds<128, 128, 3, 2, 4, 2, 1, kSplit>(p, s);
+        return launch_lds<256, 128, 3, 4, 2, 2, 1, kSplit>(p, s);
+    }
     if (p.K % 128 == 0 && p.M <= 64) {
         if (p.M <= 16) return launch_lds<16, 32, 6, 1, 1, 2, 2>(p, s);
         if (p.M <= 32) return launch_lds<32, 32, 4, 1, 1, 2, 2>(p, s);

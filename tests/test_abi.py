@@ -114,10 +114,13 @@ def test_probe_validation_without_gpu(lib):
 
 
 def test_linear_workspace_bytes(lib):
-    # 33..64 rows, K >= 4096 and a multiple of 256: 4 K slices of 64 x 128 fp32 tiles
+    # 33..256 rows, K >= 4096 and a multiple of 256: 4 K slices of fp32 tiles of
+    # 64, 128 or 256 rows x 128 columns
     assert lib.kda_linear_workspace_bytes(64, 6284, 7168) == 4 * 50 * 64 * 128 * 4
     assert lib.kda_linear_workspace_bytes(33, 128, 4096) == 4 * 64 * 128 * 4
-    for M, N, K in [(32, 6284, 7168), (65, 6284, 7168), (64, 7168, 1536), (64, 100, 4160),
+    assert lib.kda_linear_workspace_bytes(65, 6284, 7168) == 4 * 50 * 128 * 128 * 4
+    assert lib.kda_linear_workspace_bytes(256, 6284, 7168) == 4 * 50 * 256 * 128 * 4
+    for M, N, K in [(32, 6284, 7168), (257, 6284, 7168), (64, 7168, 1536), (64, 100, 4160),
                     (0, 10, 4096), (64, 0, 4096), (64, 10, 4100)]:
         assert lib.kda_linear_workspace_bytes(M, N, K) == 0, (M, N, K)
 

@@ -108,9 +108,9 @@ def test_in_proj_full_shape(rows):
     assert np.array_equal(got, again), "not deterministic"
 
 
-@pytest.mark.parametrize("rows", [33, 48, 64])
+@pytest.mark.parametrize("rows", [33, 48, 64, 65, 128, 192, 256])
 def test_in_proj_split_k(rows):
-    """33 to 64 rows with a workspace: K split over 4 slices, then the ordered sum."""
+    """33 to 256 rows with a workspace: K split over 4 slices, then the ordered sum."""
     import kimi_delta_attention_conv_amd as kda
     heads = 12
     N = 4 * 128 * heads + 128 + heads
@@ -133,7 +133,8 @@ def test_in_proj_split_k(rows):
     _check(x, w, none, ms, ns, label=f"in_proj unsplit rows={rows}")
 
 
-@pytest.mark.parametrize("M,N", [(40, 300), (64, 129), (33, 1)])
+@pytest.mark.parametrize("M,N", [(40, 300), (64, 129), (33, 1), (100, 300), (129, 130),
+                                 (256, 200)])
 def test_split_k_ragged_full(M, N):
     """Every output of a split shape whose N is not a multiple of the 128-wide tile."""
     K = 4096
