@@ -222,8 +222,9 @@ kda_status kda_verify(kda_handle h, const void* projected, int64_t pitch, int32_
  * too small a size, runs the unsplit kernel.
  * The result is deterministic for a given shape and choice of path (each
  * path sums in a fixed order; the two paths may differ in the last bit).
- * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE (M < 0, N < 1, K < 8, K not a multiple
- * of 8, a pitch too small), KDA_ERR_ALIGN (also a misaligned workspace),
+ * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE (M < 0 or > 2^20, N < 1, M N > 2^43,
+ * K < 8, K not a multiple of 8, a pitch too small), KDA_ERR_ALIGN (also a
+ * misaligned workspace),
  * KDA_ERR_HIP. M == 0 is a no-op. */
 kda_status kda_linear(const void* x, int64_t x_pitch, const void* w, void* y, int64_t y_pitch,
                       int32_t M, int32_t N, int32_t K, void* workspace, size_t workspace_bytes,

@@ -257,6 +257,9 @@ kda_status kda_linear(const void* x, int64_t x_pitch, const void* w, void* y, in
                       void* hip_stream) {
     if (M < 0 || N < 1 || K < 8 || K % 8 != 0) return KDA_ERR_SHAPE;
     if (M > (1 << 20)) return KDA_ERR_SHAPE;   // grid y limit at 64 rows a workgroup
+    // one workgroup per tile of at least 128 x 64 outputs above 64 rows: M N <= 2^43
+    // keeps every grid within 2^31 workgroups
+    if ((int64_t)M * N > ((int64_t)1 << 43)) return KDA_ERR_SHAPE;
     if (M == 0) return KDA_OK;
     if (x == nullptr || w == nullptr || y == nullptr) return KDA_ERR_NULL;
     if (x_pitch < K || y_pitch < N) return KDA_ERR_SHAPE;

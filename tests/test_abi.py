@@ -113,6 +113,19 @@ def test_probe_validation_without_gpu(lib):
     assert lib.kda_probe_sink_floats() > 0
 
 
+def test_linear_validation_without_gpu(lib):
+    fake = 0x10000   # never dereferenced: validation fails before any HIP call
+    for M, N, K, status in [(-1, 16, 64, -2), (4, 0, 64, -2), (4, 16, 60, -2), (4, 16, 0, -2),
+                            ((1 << 20) + 1, 16, 64, -2), (1 << 20, 1 << 24, 64, -2)]:
+        assert lib.kda_linear(fake, max(K, 8), fake, fake, max(N, 1), M, N, K, None, 0,
+                              None) == status, (M, N, K)
+    assert lib.kda_linear(None, 64, fake, fake, 16, 4, 16, 64, None, 0, None) == -1
+    assert lib.kda_linear(fake + 8, 64, fake, fake, 16, 4, 16, 64, None, 0, None) == -3
+    assert lib.kda_linear(fake, 64, fake, fake, 16, 4, 16, 64, fake + 4, 1024, None) == -3
+    assert lib.kda_in_proj(fake, 64, fake, fake, 16, 4, 64, 0, None, 0, None) == -2
+    assert lib.kda_o_proj(fake, 64, fake, fake, 16, 4, 5000, 64, None, 0, None) == -2
+
+
 def test_linear_workspace_bytes(lib):
     # 33..256 rows, K >= 4096 and a multiple of 256: 4 K slices of fp32 tiles of
     # 64, 128 or 256 rows x 128 columns
