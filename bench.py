@@ -421,10 +421,6 @@ def main():
     sets = [torch.as_strided(slot_base, shape, stride, off) for shape, stride, off in views]
     accepted = None if case.accepted is None else case.accepted.to(dev)
     h = core.handle
-    # one workspace serves both projections (they run in stream order)
-    ws_bytes = max(int(lib.kda_linear_workspace_bytes(S, n_in, HIDDEN)),
-                   int(lib.kda_linear_workspace_bytes(S, HIDDEN, D)))
-    work = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     pitch = case.pitch
     lib = kda.load_library()
 
