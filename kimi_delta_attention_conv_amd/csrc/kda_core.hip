@@ -110,28 +110,30 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
     // conv windows after each token in the dim-first layout: channel cl's three
     // inputs at 3 cl .. 3 cl + 2 (the global order of one head's q, k, v runs)
     __shared__ __attribute__((aligned(16))) uint16_t s_win[L][3 * N * 3];
-    __shared__ int s_dst[L];
 
-    // ---- slot resolution ([prepared] run: slots [B], or [>= B, q] + accepted)
+    // ---- slot resolution ([prepared] run: slots [B], or [>= B, q] + accepted).
+    // The accepted count and the slot row are loaded together and the carried
+    // slot is picked among the loaded values, so one round trip to memory
+    // precedes the state stream.
     const int32_t* srow = p.slots + (int64_t)r * p.slots_row_stride;
+    // unconditional load (the slot row stands in for a missing accepted array),
+    // so that it issues together with the slot loads
+    const int a_raw = *(p.accepted != nullptr ? p.accepted + r : srow);
     int dst[L];
-    bool ok = true;
+#pragma unroll
+    for (int t = 0; t < L; ++t) dst[t] = srow[t];
+    const int a = p.accepted != nullptr ? a_raw : 1;
+    bool ok = a >= 1 && a <= L;
+    int src = dst[0];
 #pragma unroll
     for (int t = 0; t < L; ++t) {
-        dst[t] = srow[t];
         ok = ok && (unsigned)dst[t] < (unsigned)p.num_slots;
-    }
-    int src = dst[0];
-    if (p.accepted != nullptr) {
-        const int a = p.accepted[r];
-        ok = ok && a >= 1 && a <= L;
-        src = ok ? srow[a - 1] : 0;
+        if (t == a - 1) src = dst[t];
     }
     if (!ok) {  // uniform across the workgroup: skip the whole request
         if (h == 0 && tid == 0) atomicAdd(p.err_count, 1);
         return;
     }
-    if (tid < L) s_dst[tid] = srow[tid];
 
     const int64_t row0 = (int64_t)r * L;
     const uint16_t* prow = p.projected + row0 * p.pitch;
@@ -339,13 +341,17 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
     // q, k and v windows are 3 runs of 128 channels x 3 bf16 = 768 B, i.e.
     // 48 chunks of 16 B each; 2-byte stores at a 6-byte stride cost far more
     // than their bytes. Issued last, after the state stores and core_out, so they
-    // do not queue ahead of the state traffic that bounds the kernel; s_win and
-    // s_dst are filled before the first barrier and never overwritten.
+    // do not queue ahead of the state traffic that bounds the kernel; s_win is
+    // filled before the first barrier and never overwritten.
     if (p.conv_dim_first16) {
         constexpr int kChunks = 3 * 48;
         for (int c = tid; c < L * kChunks; c += kThreads) {
             const int t = c / kChunks, k = c - t * kChunks, s = k / 48;
-            uint16_t* out = p.conv + (int64_t)s_dst[t] * p.conv_slot_stride +
+            int slot = dst[0];
+#pragma unroll
+            for (int u = 1; u < L; ++u)
+                if (t == u) slot = dst[u];
+            uint16_t* out = p.conv + (int64_t)slot * p.conv_slot_stride +
                             ((int64_t)s * D + (int64_t)h * N) * 3 + (k - s * 48) * 8;
             *reinterpret_cast<u32x4*>(out) = *reinterpret_cast<const u32x4*>(&s_win[t][8 * k]);
         }
