@@ -378,9 +378,9 @@ def cpu_baseline(case, seconds):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the core shards by heads and requests with no exchange; multi-GPU runs are "
-              "out of scope)", file=sys.stderr)
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the library "
+              "has no multi-GPU path: the core shards by heads and requests with no exchange, "
+              "and each GPU's share is what one process measures)", file=sys.stderr)
         sys.exit(2)
 
     import torch
