@@ -9,10 +9,11 @@
 //   docstring and stage_o: o_proj over the core rows (K = 1536 local), an
 //   MFMA GEMV with the token dimension padded to 16.
 //
-// Three kernels, chosen by the row count M and K:
+// Three GEMM kernels, chosen by the row count M and K, and a slice sum:
 //
 // Skinny (M <= 16 when K is a multiple of 64 but not of 128, up to 64 rows
-// when K is not a multiple of 64): both operands are K-contiguous (rows of X, rows of the nn.Linear weight W), so
+// when K is not a multiple of 64): both operands are K-contiguous (rows of X,
+// rows of the nn.Linear weight W), so
 // every lane reads 64 contiguous bytes of one row per 128-wide K block and
 // feeds v_mfma_f32_16x16x32_bf16 directly from registers. Within a K block,
 // lane group kg (= lane >> 4) hands K elements 8 (kg + 4q) .. +8 to MFMA K
@@ -22,8 +23,11 @@
 // wave order (a fixed order: results do not depend on timing).
 //
 // Direct-to-LDS (K a multiple of 128, or K a multiple of 64 and M > 16): BM x
-// BN tiles, X and W blocks loaded straight into a ring of LDS stages. Tiled
-// (M > 64, other K): 128 x 64 tiles staged through registers.
+// BN tiles, X and W blocks loaded straight into a ring of LDS stages; with a
+// caller's workspace and a long K (33 to 256 rows) the same kernel splits K
+// over 4 slices of workgroups and linear_split_sum adds the fp32 slices in
+// slice order. Tiled (M > 64, other K): 128 x 64 tiles staged through
+// registers.
 #include "kda_internal.h"
 
 namespace kda {
