@@ -155,3 +155,29 @@ def test_binding_fails_loudly_without_library(tmp_path):
             kda.load_library(str(tmp_path / "missing.so"))
     finally:
         kda._lib = saved
+
+
+def test_headers_are_plain_c_and_a_c_program_links(lib, tmp_path):
+    """The boundary is a C ABI: both headers compile as pedantic C99, and a C program
+    links against the library and calls its host-only entry points (no GPU call)."""
+    inc = os.path.join(ROOT, "include")
+    for path in HEADERS:
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                        "-fsyntax-only", "-x", "c", path], check=True)
+    src = tmp_path / "abi.c"
+    src.write_text(
+        '#include <string.h>\n#include "kda.h"\n#include "kda_probe.h"\n'
+        "int main(void) {\n"
+        "    kda_handle h = 0;\n"
+        "    if (kda_linear_workspace_bytes(64, 6284, 7168) != 4u * 50 * 64 * 128 * 4) return 1;\n"
+        "    if (kda_linear_workspace_bytes(512, 6284, 7168) != 0) return 2;\n"
+        "    if (strcmp(kda_status_string(KDA_OK), \"ok\") != 0) return 3;\n"
+        "    if (kda_destroy(h) != KDA_OK) return 4;\n"
+        "    if (kda_decode(h, 0, 0, 1, 0, 0, 0) != KDA_ERR_NULL) return 5;\n"
+        "    return 0;\n}\n")
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(kda.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I" + inc, str(src),
+                    "-L" + libdir, "-l:" + os.path.basename(kda.LIB_PATH),
+                    "-Wl,-rpath," + libdir, "-o", str(exe)], check=True)
+    assert subprocess.run([str(exe)]).returncode == 0
