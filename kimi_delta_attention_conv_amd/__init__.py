@@ -289,8 +289,10 @@ class KdaCore:
                       state_slot_stride=state.stride(0), num_slots=int(state.shape[0]))
         if conv.shape[0] != state.shape[0]:
             raise ValueError("conv and state pools must have the same slot count")
-        self.handle = kda_prepare(w, c, self._stream(stream))
-        torch.cuda.synchronize()   # the caller's weights may be released from here on
+        # the handle belongs to the device current at prepare time: the pools' device
+        with torch.cuda.device(self.device):
+            self.handle = kda_prepare(w, c, self._stream(stream))
+            torch.cuda.synchronize()   # the caller's weights may be released from here on
 
     def _stream(self, stream):
         if stream is None:
