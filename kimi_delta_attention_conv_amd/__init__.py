@@ -208,8 +208,9 @@ def linear(x, w, y=None, stream=None, workspace="auto"):
         raise TypeError("workspace must be a contiguous tensor on x's GPU")
     ws_ptr = 0 if workspace is None else workspace.data_ptr()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    kda_linear(x.data_ptr(), x.stride(0), w.data_ptr(), y.data_ptr(), y.stride(0), M, N, K,
-               ws_ptr, ws_bytes, _stream_of(stream))
+    with torch.cuda.device(x.device):   # launch on the tensors' device (its current stream)
+        kda_linear(x.data_ptr(), x.stride(0), w.data_ptr(), y.data_ptr(), y.stride(0), M, N, K,
+                   ws_ptr, ws_bytes, _stream_of(stream))
     return y
 
 

@@ -174,3 +174,21 @@ def test_validation():
     kda.kda_linear(0, 64, 0, 0, 16, 0, 16, 64)   # M == 0: no-op
     torch.cuda.synchronize()
     assert torch.all(y == 0)
+
+
+def test_torch_helper_matches_the_abi_call():
+    """kimi_delta_attention_conv_amd.linear (torch tensors, a workspace allocated on
+    demand) gives the same bits as kda_linear called directly with the same choice
+    of path, and passes workspace=None through to the unsplit kernel."""
+    import kimi_delta_attention_conv_amd as kda
+    M, N, K = 48, 300, 4096
+    x, w = make_linear(M, N, K, seed=77)
+    direct_split = _run(x, w, workspace="auto")
+    direct_plain = _run(x, w)
+    got_split = bf16_np(kda.linear(x.cuda(), w.cuda()).cpu())
+    got_plain = bf16_np(kda.linear(x.cuda(), w.cuda(), workspace=None).cpu())
+    torch.cuda.synchronize()
+    assert np.array_equal(got_split, direct_split)
+    assert np.array_equal(got_plain, direct_plain)
+    with pytest.raises(ValueError):
+        kda.linear(x.cuda(), w.cuda(), workspace="bogus")
