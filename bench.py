@@ -19,7 +19,9 @@ Metric bytes per step (state + conv window, read once per request and written
 once per token): (R + S) x H x 67,840 B, where a unit of 67,840 B is one
 128 x 128 fp32 state tile plus one 3 x 384 bf16 conv window.
 
-Prints one JSON line. `--config N` selects another workload (0..4) for
+Prints one JSON line. The default run also times the large decode batch
+(R = 256, L = 1, four disjoint slot sets rotating; kernel time only) and adds it
+under `decode_r256`. `--config N` selects another workload (0..4) for
 exploration; `--probe` adds the plain read / write / copy HBM probes.
 """
 from __future__ import annotations
@@ -54,6 +56,9 @@ def parse_args():
     ap.add_argument("--probe", action="store_true",
                     help="run the HBM probes (the default; kept for older command lines)")
     ap.add_argument("--no-probe", action="store_true", help="skip the HBM probes")
+    ap.add_argument("--skip-decode", action="store_true",
+                    help="with the default workload, skip the decode R=256 timing that the "
+                         "line also carries")
     ap.add_argument("--probe-only", action="store_true",
                     help="run only the HBM probes (counter calibration)")
     ap.add_argument("--graph", type=int, default=0, metavar="CHAIN",
@@ -95,6 +100,64 @@ def rotation_sets(case, torch):
     shape, stride = tuple(case.slots.shape), tuple(case.slots.contiguous().stride())
     views = [(shape, stride, k * S) for k in range(len(chunks))]
     return torch.cat(chunks).contiguous(), views
+
+
+def time_workload(torch, kda, index, steps, warmup):
+    """Kernel time of one more workload on the current stream (HIP events over
+    `steps` launches after `warmup`, slot sets rotating as in the main run);
+    returns its tokens/s, metric GB/s and fraction of the HBM peak."""
+    from kda_inputs import make_config
+
+    case = make_config(index)
+    dev = "cuda"
+    conv_storage = case.conv_storage.to(dev)
+    conv = conv_storage if case.conv_dim_first else conv_storage.transpose(-1, -2)
+    state = case.state.to(dev)
+    core = kda.KdaCore(conv_weight=case.conv_weight.to(dev),
+                       conv_bias=None if case.conv_bias is None else case.conv_bias.to(dev),
+                       f_b=case.f_b.to(dev), A_log=case.A_log.to(dev),
+                       dt_bias=case.dt_bias.to(dev), norm_weight=case.norm_weight.to(dev),
+                       gate_lower_bound=case.gate_lower_bound, norm_eps=case.norm_eps,
+                       l2_eps=case.l2_eps, conv=conv, state=state)
+    projected = case.projected.to(dev)
+    out = torch.empty(case.S, case.D, dtype=torch.bfloat16, device=dev)
+    slot_base, views = rotation_sets(case, torch)
+    slot_base = slot_base.to(dev)
+    sets = [torch.as_strided(slot_base, shape, stride, off) for shape, stride, off in views]
+    accepted = None if case.accepted is None else case.accepted.to(dev)
+    lib = kda.load_library()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def launch(i):
+        s = sets[i % len(sets)]
+        if accepted is None:
+            return lib.kda_decode(core.handle, projected.data_ptr(), case.pitch, case.R,
+                                  s.data_ptr(), out.data_ptr(), sp)
+        return lib.kda_verify(core.handle, projected.data_ptr(), case.pitch, case.R, case.L,
+                              s.data_ptr(), s.stride(0), accepted.data_ptr(), out.data_ptr(), sp)
+
+    for i in range(warmup):
+        if launch(i) != 0:
+            raise RuntimeError(f"{case.name}: launch failed")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        launch(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    if core.device_errors():
+        raise RuntimeError(f"{case.name}: requests were skipped for invalid slots")
+    kernel_ms = e0.elapsed_time(e1) / steps
+    metric_bytes = (case.R + case.S) * case.H * UNIT_BYTES
+    gbps = metric_bytes / (kernel_ms * 1e-3) / 1e9
+    core.close()
+    return {"workload": case.name, "requests": case.R, "tokens": case.L,
+            "tokens_per_s": round(case.S / (kernel_ms * 1e-3), 1),
+            "kernel_ms": round(kernel_ms, 5), "gbps": round(gbps, 1),
+            "frac": round(gbps / HBM_PEAK_GBPS, 4), "metric_bytes_per_step": metric_bytes,
+            "slot_sets_rotated": len(sets), "steps": steps, "warmup": warmup}
 
 
 def probe(torch, kda):
@@ -555,6 +618,11 @@ def main():
     core.close()
     del state, conv_storage
     torch.cuda.empty_cache()
+    if args.config == 3 and not args.graph and not args.skip_decode:
+        # the other workload the HBM target is stated for, kernel time only
+        print("[bench] decode R=256", file=sys.stderr, flush=True)
+        result["decode_r256"] = time_workload(torch, kda, 4, 100, 10)
+        torch.cuda.empty_cache()
     if args.cpu_seconds > 0:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
