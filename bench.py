@@ -102,6 +102,37 @@ def rotation_sets(case, torch):
     return torch.cat(chunks).contiguous(), views
 
 
+def time_pattern(torch, lib, state, case, sets, accepted, steps, warmup):
+    """The core's state traffic alone (kda_probe_state_stream: same grid, slots,
+    tile loads and per-token stores, no arithmetic, no conv windows) over the
+    same rotating slot sets: the ceiling of the kernel's access pattern."""
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    stride = case.H * 128 * 128
+
+    def launch(i):
+        s = sets[i % len(sets)]
+        return lib.kda_probe_state_stream(state.data_ptr(), stride, case.num_slots, s.data_ptr(),
+                                          s.stride(0) if s.dim() == 2 else 1,
+                                          None if accepted is None else accepted.data_ptr(),
+                                          case.R, case.L, case.H, sp)
+
+    for i in range(warmup):
+        if launch(i) != 0:
+            raise RuntimeError("state stream probe failed")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        launch(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    state_bytes = (case.R + case.S) * case.H * 128 * 128 * 4
+    return {"kernel_ms": round(ms, 5), "state_bytes": state_bytes,
+            "gbps": round(state_bytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def time_workload(torch, kda, index, steps, warmup):
     """Kernel time of one more workload on the current stream (HIP events over
     `steps` launches after `warmup`, slot sets rotating as in the main run);
@@ -153,10 +184,13 @@ def time_workload(torch, kda, index, steps, warmup):
     metric_bytes = (case.R + case.S) * case.H * UNIT_BYTES
     gbps = metric_bytes / (kernel_ms * 1e-3) / 1e9
     core.close()
+    pattern = time_pattern(torch, lib, state, case, sets, accepted, steps, warmup)
     return {"workload": case.name, "requests": case.R, "tokens": case.L,
             "tokens_per_s": round(case.S / (kernel_ms * 1e-3), 1),
             "kernel_ms": round(kernel_ms, 5), "gbps": round(gbps, 1),
             "frac": round(gbps / HBM_PEAK_GBPS, 4), "metric_bytes_per_step": metric_bytes,
+            "pattern_probe": pattern,
+            "frac_of_pattern": round(pattern["kernel_ms"] / kernel_ms, 4),
             "slot_sets_rotated": len(sets), "steps": steps, "warmup": warmup}
 
 
@@ -607,6 +641,11 @@ def main():
     if launch_us is not None:
         result["launch_us"] = launch_us
         result["hot"] = hot
+    if not args.graph:
+        # the kernel against its own access pattern with no arithmetic (time ratio)
+        pattern = time_pattern(torch, lib, state, case, sets, accepted, min(args.steps, 100), 10)
+        result["roofline"]["pattern_probe"] = pattern
+        result["roofline"]["frac_of_pattern"] = round(pattern["kernel_ms"] / kernel_ms, 4)
     if not args.no_probe:
         print("[bench] HBM probes", file=sys.stderr, flush=True)
         pr = probe(torch, kda)

@@ -106,8 +106,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_probe_read.argtypes = [vp, i64, vp, vp]
     lib.kda_probe_copy_runs.argtypes = [vp, vp, i64, vp]
     lib.kda_probe_write_runs.argtypes = [vp, i64, ctypes.c_float, vp]
+    lib.kda_probe_state_stream.argtypes = [vp, i64, i32, vp, i64, vp, i32, i32, i32, vp]
     for f in (lib.kda_probe_copy, lib.kda_probe_write, lib.kda_probe_read, lib.kda_probe_copy_runs,
-              lib.kda_probe_write_runs):
+              lib.kda_probe_write_runs, lib.kda_probe_state_stream):
         f.restype = ctypes.c_int
     lib.kda_probe_sink_floats.argtypes = []
     lib.kda_probe_sink_floats.restype = i32

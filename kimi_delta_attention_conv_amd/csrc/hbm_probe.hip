@@ -1,8 +1,9 @@
 // HBM stream probes (measurement only; see include/kda_probe.h): grid-stride
 // read, write and copy with 16-byte non-temporal accesses, sized to keep every
-// CU's memory pipeline busy (256 CUs x 8 workgroups of 256 threads), and write
+// CU's memory pipeline busy (256 CUs x 8 workgroups of 256 threads), write
 // and copy over one contiguous run per workgroup with plain stores (4096
-// workgroups of 256 threads), the fastest write shape measured on MI355X.
+// workgroups of 256 threads), the fastest write shape measured on MI355X, and
+// the core kernel's state traffic with none of its arithmetic.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -69,6 +70,69 @@ __global__ __launch_bounds__(kThreads) void probe_copy_runs(f32x4* __restrict__ 
     for (int64_t i = lo + threadIdx.x; i < hi; i += kThreads) dst[i] = src[i];
 }
 
+// The core kernel's state traffic alone (kda_probe_state_stream): one
+// workgroup of 512 threads per (request, head) unit, units blocked by XCD
+// (workgroup b runs on XCD b % 8), wave w holding tile rows 16w .. 16w + 15 as
+// the core does (lane l: rows 16w + (l >> 3) and 16w + 8 + (l >> 3), columns
+// 32m + 4(l & 7) .. +3), non-temporal loads for one token and plain loads
+// otherwise, non-temporal stores, one tile written per token.
+constexpr int kTile = 128;
+template <int L>
+__global__ __launch_bounds__(512) void probe_state_stream(float* __restrict__ state,
+                                                          int64_t slot_stride, int num_slots,
+                                                          const int32_t* __restrict__ slots,
+                                                          int64_t row_stride,
+                                                          const int32_t* __restrict__ accepted,
+                                                          int requests, int heads) {
+    int unit = blockIdx.x;
+    const int q = (requests * heads) >> 3;
+    if ((int)blockIdx.x < 8 * q) unit = (blockIdx.x & 7) * q + (blockIdx.x >> 3);
+    const int r = unit / heads, h = unit - r * heads;
+    const int32_t* srow = slots + (int64_t)r * row_stride;
+    const int a = accepted != nullptr ? accepted[r] : 1;
+    int dst[L];
+    bool ok = a >= 1 && a <= L;
+    int src = srow[0];
+#pragma unroll
+    for (int t = 0; t < L; ++t) {
+        dst[t] = srow[t];
+        ok = ok && (unsigned)dst[t] < (unsigned)num_slots;
+        if (t == a - 1) src = dst[t];
+    }
+    if (!ok) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t off = (int64_t)h * kTile * kTile + (int64_t)(wave * 16 + (lane >> 3)) * kTile +
+                        (lane & 7) * 4;
+    f32x4 S[2][4];
+    const float* sb = state + (int64_t)src * slot_stride + off;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const f32x4* ptr = reinterpret_cast<const f32x4*>(sb + g * 8 * kTile + 32 * m);
+            S[g][m] = (L == 1) ? __builtin_nontemporal_load(ptr) : *ptr;
+        }
+#pragma unroll
+    for (int t = 0; t < L; ++t) {
+        float* dp = state + (int64_t)dst[t] * slot_stride + off;
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                S[g][m] *= 0.999f;
+                __builtin_nontemporal_store(S[g][m], reinterpret_cast<f32x4*>(dp + g * 8 * kTile + 32 * m));
+            }
+    }
+}
+
+template <int L>
+void launch_state_stream(float* state, int64_t slot_stride, int num_slots, const int32_t* slots,
+                         int64_t row_stride, const int32_t* accepted, int requests, int heads,
+                         hipStream_t s) {
+    hipLaunchKernelGGL(probe_state_stream<L>, dim3((unsigned)(requests * heads)), dim3(512), 0, s,
+                       state, slot_stride, num_slots, slots, row_stride, accepted, requests, heads);
+}
+
 constexpr int kRunBlocks = 4096;
 
 bool ok16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -116,6 +180,32 @@ int kda_probe_copy_runs(void* dst, const void* src, int64_t bytes, void* hip_str
     hipLaunchKernelGGL(probe_copy_runs, dim3(kRunBlocks), dim3(kThreads), 0,
                        static_cast<hipStream_t>(hip_stream), static_cast<f32x4*>(dst),
                        static_cast<const f32x4*>(src), n, per);
+    return launched();
+}
+
+int kda_probe_state_stream(float* state, int64_t state_slot_stride, int32_t num_slots,
+                           const int32_t* slots, int64_t slots_row_stride,
+                           const int32_t* accepted, int32_t requests, int32_t tokens,
+                           int32_t heads, void* hip_stream) {
+    if (tokens < 1 || tokens > 8 || heads < 1 || heads > 4096 || requests < 0 ||
+        num_slots < 1 || slots_row_stride < tokens)
+        return KDA_ERR_SHAPE;
+    if ((int64_t)requests * heads > INT32_MAX) return KDA_ERR_SHAPE;
+    if (state_slot_stride < (int64_t)heads * kTile * kTile) return KDA_ERR_SHAPE;
+    if (requests == 0) return KDA_OK;
+    if (state == nullptr || slots == nullptr) return KDA_ERR_NULL;
+    if (!ok16(state) || state_slot_stride % 4 != 0 ||
+        (reinterpret_cast<uintptr_t>(slots) & 3) != 0 ||
+        (reinterpret_cast<uintptr_t>(accepted) & 3) != 0)
+        return KDA_ERR_ALIGN;
+    using Launch = void (*)(float*, int64_t, int, const int32_t*, int64_t, const int32_t*, int,
+                            int, hipStream_t);
+    static const Launch kLaunch[8] = {launch_state_stream<1>, launch_state_stream<2>,
+                                      launch_state_stream<3>, launch_state_stream<4>,
+                                      launch_state_stream<5>, launch_state_stream<6>,
+                                      launch_state_stream<7>, launch_state_stream<8>};
+    kLaunch[tokens - 1](state, state_slot_stride, num_slots, slots, slots_row_stride, accepted,
+                        requests, heads, static_cast<hipStream_t>(hip_stream));
     return launched();
 }
 

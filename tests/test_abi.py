@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("kda_prepare", "kda_decode", "kda_verify", "kda_device_errors", "kda_destroy",
               "kda_status_string", "kda_last_hip_error", "kda_probe_copy", "kda_probe_write",
-              "kda_probe_read", "kda_probe_sink_floats"):
+              "kda_probe_read", "kda_probe_sink_floats", "kda_probe_state_stream"):
         assert n in names, n
 
 
@@ -111,6 +111,29 @@ def test_probe_validation_without_gpu(lib):
     assert lib.kda_probe_copy_runs(0x1000, None, 16, None) == -1
     assert lib.kda_probe_write_runs(0x1000, 20, 1.0, None) == -3
     assert lib.kda_probe_sink_floats() > 0
+
+
+def test_state_stream_probe_validation_without_gpu(lib):
+    fake = 0x10000   # never dereferenced: validation fails before any HIP call
+    tile = 128 * 128
+    call = lambda state=fake, stride=12 * tile, slots_n=16, slots=fake, rs=8, acc=fake, R=4, L=8, \
+        H=12: lib.kda_probe_state_stream(state, stride, slots_n, slots, rs, acc, R, L, H, None)
+    assert call(L=0) == -2
+    assert call(L=9) == -2
+    assert call(H=0) == -2
+    assert call(H=4097) == -2
+    assert call(R=-1) == -2
+    assert call(slots_n=0) == -2
+    assert call(rs=7) == -2
+    assert call(stride=12 * tile - 4) == -2
+    assert call(R=1 << 20, H=4096) == -2
+    assert call(R=0) == 0                  # nothing to do, nothing enqueued
+    assert call(state=None) == -1
+    assert call(slots=None) == -1
+    assert call(state=fake + 8) == -3
+    assert call(stride=12 * tile + 2) == -3
+    assert call(slots=fake + 2) == -3
+    assert call(acc=fake + 1) == -3
 
 
 def test_linear_validation_without_gpu(lib):
