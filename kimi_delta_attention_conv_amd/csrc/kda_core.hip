@@ -207,6 +207,16 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
     const int rsub = lane >> 3;
     const int csub = (lane & 7) * 4;
     const int64_t unit_off = (int64_t)h * N * N + (int64_t)(wave * 16 + rsub) * N + csub;
+    // A bare barrier (no fence, no wait for data) before the state stream: every
+    // wave's small loads above enter the CU's memory pipeline ahead of any
+    // wave's 8 KiB share of the tile. Without it, the waves issued last (the v
+    // conv and gate waves) find their conv and gate inputs queued behind the
+    // other waves' state loads, and the first barrier below waits for them
+    // (measured 3 % slower for the 64 x 8 verify batch on MI355X). The early
+    // return above is uniform across the workgroup, so every wave arrives here.
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
     f32x4 S[2][4];
     {
         const float* sb = p.state + (int64_t)src * p.state_slot_stride + unit_off;
