@@ -25,8 +25,7 @@
  *              PreparedKda.__init__ (weights, fp32 norm weight, the scalars
  *              gate_lower_bound, 128^-0.5, o_norm.eps), _operands (the packed
  *              projection row and the operand set), prepare_caches and run
- *              (decode: slots [B]; verify: slots [>= B, q], accepted [>= B]),
- *              decode_conv_weight ([3D, 1, W] -> [3, W, D]).
+ *              (decode: slots [B]; verify: slots [>= B, q], accepted [>= B]).
  *
  * Conventions for every entry point:
  *   - Pointers marked "device" are HIP device pointers on the device that is
@@ -102,8 +101,8 @@ typedef struct {
     int32_t heads;            /* H >= 1 heads of 128 channels; D = 128 H */
     int32_t conv_width;       /* W; must be KDA_CONV_WIDTH */
     const void* conv_weight;  /* bf16 [3D][1][W], the nn.Conv1d layout (q, k, v channel
-                                 blocks of D); re-laid as [3][W][D] fp32
-                                 ([prepared] decode_conv_weight). 2-byte aligned. */
+                                 blocks of D); kept in that order as fp32 in the
+                                 handle. 2-byte aligned. */
     const void* conv_bias;    /* bf16 [3D], or NULL for no conv bias (taken as zero) */
     const void* f_b;          /* bf16 [D][128], row i = output channel i. 2-byte aligned. */
     const void* A_log;        /* [H], one per head ([prepared]: heads = A_log.numel());
@@ -147,8 +146,8 @@ typedef struct {
 } kda_caches;
 
 /* Creates a handle: validates, allocates the handle's device memory, re-lays
- * the weights out on `hip_stream` ([prepared] PreparedKda.__init__ and
- * decode_conv_weight) and records the caches. *out is set only on KDA_OK.
+ * the weights out on `hip_stream` ([prepared] PreparedKda.__init__) and records
+ * the caches. *out is set only on KDA_OK.
  * Errors: KDA_ERR_NULL (w, c, out, a weight or cache pointer), KDA_ERR_SHAPE
  * (heads < 1, num_slots < 1, a stride too small or negative, norm_head_stride
  * not 0 or 128, a non-finite scalar or negative epsilon, rounding not a

@@ -15,7 +15,7 @@ constexpr int kThreads = 512;   // 8 waves of 64: wave w owns state rows 16w .. 
 
 // Weights in the layout the core kernel reads, owned by a handle.
 struct PreparedWeights {
-    float* conv_w;        // fp32 [3][W][D]: tap j of channel (s, d) at (s * W + j) * D + d
+    float* conv_w;        // fp32 [3D][W]: tap j of channel c at c * W + j (one 16-byte row a channel)
     float* conv_b;        // fp32 [3D] (zeros when the layer has no conv bias)
     uint16_t* f_b;        // bf16 [D][128]
     float* a_exp;         // fp32 [H] = exp(A_log)
