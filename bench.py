@@ -123,10 +123,11 @@ def time_pattern(torch, lib, state, case, sets, accepted, steps, warmup):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    for i in range(steps):
-        launch(warmup + i)
+    failed = sum(launch(warmup + i) != 0 for i in range(steps))
     e1.record(stream)
     torch.cuda.synchronize()
+    if failed:
+        raise RuntimeError(f"state stream probe: {failed} launches failed")
     ms = e0.elapsed_time(e1) / steps
     state_bytes = (case.R + case.S) * case.H * 128 * 128 * 4
     return {"kernel_ms": round(ms, 5), "state_bytes": state_bytes,
@@ -174,10 +175,11 @@ def time_workload(torch, kda, index, steps, warmup):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    for i in range(steps):
-        launch(warmup + i)
+    failed = sum(launch(warmup + i) != 0 for i in range(steps))
     e1.record(stream)
     torch.cuda.synchronize()
+    if failed:
+        raise RuntimeError(f"{case.name}: {failed} launches failed")
     if core.device_errors():
         raise RuntimeError(f"{case.name}: requests were skipped for invalid slots")
     kernel_ms = e0.elapsed_time(e1) / steps
