@@ -560,11 +560,12 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
-    for i in range(args.steps):
-        launches[(args.warmup + i) % len(launches)]()
+    failed = sum(launches[(args.warmup + i) % len(launches)]() != 0 for i in range(args.steps))
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if failed:
+        raise RuntimeError(f"{failed} timed launches failed")
     gpu_ms = e0.elapsed_time(e1)
     errors = core.device_errors()
     if errors:
