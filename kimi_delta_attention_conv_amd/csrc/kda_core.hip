@@ -11,17 +11,18 @@
 //              PreparedKda._operands (packed projection row), PreparedKda.__init__
 //              (weights prepared once: fp32 norm weight, exp of A_log).
 //
-// One workgroup owns one (request, head) unit for all L tokens: 512 threads,
-// wave w holds state rows v = 16w .. 16w + 15 in registers across the token
+// One workgroup owns one (request, head) unit for all L tokens: 8 waves of 64,
+// wave w holding state rows v = 16w .. 16w + 15 in registers across the token
 // loop (the pages split a head into eight 16-row v-chunks on separate CTAs
 // that trade q/k and norm partials through mailboxes; here the eight chunks
 // are the eight waves of one workgroup and the hand-offs go through LDS).
+// Grids of at most one unit a CU use 16 waves of 8 rows instead.
 //
 // Lane layout of the state: lane l of wave w holds rows 16w + (l >> 3) and
-// 16w + 8 + (l >> 3), columns 32m + 4(l & 7) .. +3 for m = 0..3. One dwordx4
-// load or store instruction therefore covers eight full 128-byte lines
-// (eight rows x 128 B), and a row's dot product is an 8-lane reduction done
-// with three DPP steps.
+// 16w + 8 + (l >> 3) (16 waves: row 8w + (l >> 3)), columns 32m + 4(l & 7) ..
+// +3 for m = 0..3. One dwordx4 load or store instruction therefore covers
+// eight full 128-byte lines (eight rows x 128 B), and a row's dot product is
+// an 8-lane reduction done with three DPP steps.
 #include "kda_internal.h"
 
 namespace kda {
@@ -84,9 +85,13 @@ __device__ __forceinline__ float dot4(f32x4 a, f32x4 b, float acc) {
     return acc;
 }
 
-template <int L>
-__global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) {
+template <int L, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void kda_core_kernel(const CoreParams p) {
+    static_assert(WAVES == 8 || WAVES == 16, "8 or 16 waves a (request, head) unit");
     constexpr int N = kHeadDim;
+    constexpr int RW = N / WAVES;        // state rows a wave holds: 16 or 8
+    constexpr int G = RW / 8;            // 8-row groups a lane holds: 2 or 1
+    constexpr int NT = 64 * WAVES;
     const int H = p.heads;
     const int D = H * N;
     // XCD-blocked unit order: the dispatcher sends workgroup b to XCD b % 8, so
@@ -141,6 +146,7 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
 
     // ---- small inputs first: conv window + x (waves 0-5), gate + beta (6-7)
     const bool conv_thread = tid < 3 * N;
+    const bool gate_thread = !conv_thread && (WAVES == 8 || tid < 4 * N);   // 16 waves: 8-15 neither
     const int cl = conv_thread ? tid : tid - 3 * N;   // conv channel, or gate column
     const int cs = cl >> 7;                           // 0 q, 1 k, 2 v
     const int cj = cl & (N - 1);
@@ -162,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
         const f32x4 w4 = *reinterpret_cast<const f32x4*>(p.conv_w + cch * kWidth);
         cw[0] = w4.x; cw[1] = w4.y; cw[2] = w4.z; cw[3] = w4.w;
         cb = p.conv_b[cch];
-    } else {
+    } else if (gate_thread) {
 #pragma unroll
         for (int t = 0; t < L; ++t) xb[t] = prow[t * p.pitch + 3 * (int64_t)D + (int64_t)h * N + cj];
         // unconditional (clamped row): a load under a per-lane branch here makes
@@ -171,19 +177,23 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
         braw = prow[min(cj, L - 1) * p.pitch + 4 * (int64_t)D + kFaRank + h];
     }
 
-    // ---- gate MFMA operands: wave w computes outputs 16w .. 16w + 15 of the head
+    // ---- gate MFMA operands: wave w < 8 computes outputs 16w .. 16w + 15 of the head
+    const bool mfma_wave = WAVES == 8 || wave < 8;
     const int mn = lane & 15;        // A row (token) / B column (output)
     const int kg = lane >> 4;        // which 8 of each 32-wide K step
-    const int i_out = wave * 16 + mn;
+    const int i_out = (WAVES == 8 ? wave : (wave & 7)) * 16 + mn;
     bf16x8 bfrag[4];
-    {
+    if (mfma_wave) {
         const uint16_t* fb = p.f_b + (int64_t)(h * N + i_out) * kFaRank + 8 * kg;
 #pragma unroll
         for (int s = 0; s < 4; ++s)
             bfrag[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(fb + 32 * s));
+    } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bfrag[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
     bf16x8 afrag[4];
-    if (mn < L) {   // rows are only 4-byte aligned: dword loads
+    if (mfma_wave && mn < L) {   // rows are only 4-byte aligned: dword loads
         const uint32_t* fa = reinterpret_cast<const uint32_t*>(prow + mn * p.pitch + 4 * (int64_t)D + 8 * kg);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -194,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
 #pragma unroll
         for (int s = 0; s < 4; ++s) afrag[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
-    const float dtv = p.dt_bias[h * N + i_out];
+    const float dtv = mfma_wave ? p.dt_bias[h * N + i_out] : 0.0f;
     const float aexp = p.a_exp[h];
     float nw0 = 0.0f, nw1 = 0.0f;
     if (wave < L) {
@@ -209,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
     // plain loads measured faster on MI355X.
     const int rsub = lane >> 3;
     const int csub = (lane & 7) * 4;
-    const int64_t unit_off = (int64_t)h * N * N + (int64_t)(wave * 16 + rsub) * N + csub;
+    const int64_t unit_off = (int64_t)h * N * N + (int64_t)(wave * RW + rsub) * N + csub;
     // A bare barrier (no fence, no wait for data) before the state stream: every
     // wave's small loads above enter the CU's memory pipeline ahead of any
     // wave's 8 KiB share of the tile. Without it, the waves issued last (the v
@@ -220,11 +230,11 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
-    f32x4 S[2][4];
+    f32x4 S[G][4];
     {
         const float* sb = p.state + (int64_t)src * p.state_slot_stride + unit_off;
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
+        for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const f32x4* ptr = reinterpret_cast<const f32x4*>(sb + g * 8 * N + 32 * m);
@@ -258,14 +268,14 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
                 cw_out[2 * p.conv_pos_stride] = (uint16_t)b2;
             }
         }
-    } else {
+    } else if (gate_thread) {
 #pragma unroll
         for (int t = 0; t < L; ++t) s_gate[t][cj] = bf16_to_f32(xb[t]);
         if (cj < L) s_braw[cj] = bf16_to_f32(braw);
     }
 
     // ---- g1 = f_b f_a on MFMA (tokens padded to 16), then the lower-bound gate
-    {
+    if (mfma_wave) {
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
@@ -311,8 +321,8 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
         const float beta = sigmoid(s_braw[t]);
         float* dp = p.state + (int64_t)dst[t] * p.state_slot_stride + unit_off;
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            const int row = wave * 16 + g * 8 + rsub;
+        for (int g = 0; g < G; ++g) {
+            const int row = wave * RW + g * 8 + rsub;
             float a = 0.0f, b = 0.0f;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
@@ -358,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void kda_core_kernel(const CoreParams p) 
     // filled before the first barrier and never overwritten.
     if (p.conv_dim_first16) {
         constexpr int kChunks = 3 * 48;
-        for (int c = tid; c < L * kChunks; c += kThreads) {
+        for (int c = tid; c < L * kChunks; c += NT) {
             const int t = c / kChunks, k = c - t * kChunks, s = k / 48;
             int slot = dst[0];
 #pragma unroll
@@ -420,10 +430,18 @@ __global__ void kda_prepare_kernel(const PrepareParams in, const PreparedWeights
     }
 }
 
+// Up to one unit a CU, a unit's eight 16-row waves leave its per-token
+// arithmetic exposed between store bursts; sixteen 8-row waves halve each
+// wave's chain. Larger grids keep 2 eight-wave units a CU resident.
+constexpr int64_t kSmallGrid = 256;   // MI355X compute units
+
 template <int L>
 hipError_t launch_core_t(const CoreParams& p, hipStream_t s) {
-    const dim3 grid((unsigned)(p.requests * p.heads)), block(kThreads);
-    hipLaunchKernelGGL(kda_core_kernel<L>, grid, block, 0, s, p);
+    const dim3 grid((unsigned)(p.requests * p.heads));
+    if ((int64_t)p.requests * p.heads <= kSmallGrid)
+        hipLaunchKernelGGL((kda_core_kernel<L, 16>), grid, dim3(1024), 0, s, p);
+    else
+        hipLaunchKernelGGL((kda_core_kernel<L, 8>), grid, dim3(512), 0, s, p);
     return hipGetLastError();
 }
 

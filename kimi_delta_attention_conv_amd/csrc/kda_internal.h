@@ -11,7 +11,6 @@ constexpr int kHeadDim = 128;   // dk = dv
 constexpr int kFaRank = 128;    // f_a width
 constexpr int kWidth = 4;       // conv taps
 constexpr int kMaxTokens = 8;   // verify length bound
-constexpr int kThreads = 512;   // 8 waves of 64: wave w owns state rows 16w .. 16w + 15
 
 // Weights in the layout the core kernel reads, owned by a handle.
 struct PreparedWeights {
