@@ -43,9 +43,9 @@ int kda_probe_read(const void* src, int64_t bytes, float* sink, void* hip_stream
 int32_t kda_probe_sink_floats(void);
 
 /* The state traffic of kda_decode / kda_verify alone, for the ceiling of that
- * access pattern: the core kernel's grid (one 512-thread workgroup per
- * (request, head), the same order of units over the XCDs), its lane layout
- * and its load and store flavours, and no other work. Workgroup (r, h) reads
+ * access pattern: the core kernel's grid (one workgroup per (request, head)
+ * with the core's 8 or 16 waves, the same order of units over the XCDs), its
+ * lane layout and its load and store flavours, and no other work. Workgroup (r, h) reads
  * the 64 KiB fp32 tile state[src][h] and, for t = 0 .. tokens-1, writes
  * c^(t+1) times it to state[dst[t]][h], c = 0.999f applied once per token in
  * fp32. Slots as in kda_verify: dst[t] = slots[r * slots_row_stride + t],

@@ -71,14 +71,15 @@ __global__ __launch_bounds__(kThreads) void probe_copy_runs(f32x4* __restrict__ 
 }
 
 // The core kernel's state traffic alone (kda_probe_state_stream): one
-// workgroup of 512 threads per (request, head) unit, units blocked by XCD
-// (workgroup b runs on XCD b % 8), wave w holding tile rows 16w .. 16w + 15 as
-// the core does (lane l: rows 16w + (l >> 3) and 16w + 8 + (l >> 3), columns
-// 32m + 4(l & 7) .. +3), non-temporal loads for one token and plain loads
-// otherwise, non-temporal stores, one tile written per token.
+// workgroup per (request, head) unit with the core's waves a unit, units
+// blocked by XCD (workgroup b runs on XCD b % 8), the core's lane layout (8
+// waves: lane l holds rows 16w + (l >> 3) and 16w + 8 + (l >> 3); 16 waves:
+// row 8w + (l >> 3); columns 32m + 4(l & 7) .. +3), non-temporal loads for one
+// token and plain loads otherwise, non-temporal stores, one tile written per
+// token.
 constexpr int kTile = 128;
-template <int L>
-__global__ __launch_bounds__(512) void probe_state_stream(float* __restrict__ state,
+template <int L, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void probe_state_stream(float* __restrict__ state,
                                                           int64_t slot_stride, int num_slots,
                                                           const int32_t* __restrict__ slots,
                                                           int64_t row_stride,
@@ -100,13 +101,14 @@ __global__ __launch_bounds__(512) void probe_state_stream(float* __restrict__ st
         if (t == a - 1) src = dst[t];
     }
     if (!ok) return;
+    constexpr int RW = kTile / WAVES, G = RW / 8;   // rows a wave, 8-row groups a lane
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t off = (int64_t)h * kTile * kTile + (int64_t)(wave * 16 + (lane >> 3)) * kTile +
+    const int64_t off = (int64_t)h * kTile * kTile + (int64_t)(wave * RW + (lane >> 3)) * kTile +
                         (lane & 7) * 4;
-    f32x4 S[2][4];
+    f32x4 S[G][4];
     const float* sb = state + (int64_t)src * slot_stride + off;
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const f32x4* ptr = reinterpret_cast<const f32x4*>(sb + g * 8 * kTile + 32 * m);
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(512) void probe_state_stream(float* __restrict__ st
     for (int t = 0; t < L; ++t) {
         float* dp = state + (int64_t)dst[t] * slot_stride + off;
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
+        for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 S[g][m] *= 0.999f;
@@ -125,12 +127,19 @@ __global__ __launch_bounds__(512) void probe_state_stream(float* __restrict__ st
     }
 }
 
+// The core kernel's choice of waves a unit: 16 for one token or at most 256
+// units, else 8.
 template <int L>
 void launch_state_stream(float* state, int64_t slot_stride, int num_slots, const int32_t* slots,
                          int64_t row_stride, const int32_t* accepted, int requests, int heads,
                          hipStream_t s) {
-    hipLaunchKernelGGL(probe_state_stream<L>, dim3((unsigned)(requests * heads)), dim3(512), 0, s,
-                       state, slot_stride, num_slots, slots, row_stride, accepted, requests, heads);
+    const dim3 grid((unsigned)(requests * heads));
+    if (L == 1 || (int64_t)requests * heads <= 256)
+        hipLaunchKernelGGL((probe_state_stream<L, 16>), grid, dim3(1024), 0, s, state, slot_stride,
+                           num_slots, slots, row_stride, accepted, requests, heads);
+    else
+        hipLaunchKernelGGL((probe_state_stream<L, 8>), grid, dim3(512), 0, s, state, slot_stride,
+                           num_slots, slots, row_stride, accepted, requests, heads);
 }
 
 constexpr int kRunBlocks = 4096;

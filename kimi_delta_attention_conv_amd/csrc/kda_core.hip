@@ -16,7 +16,7 @@
 // loop (the pages split a head into eight 16-row v-chunks on separate CTAs
 // that trade q/k and norm partials through mailboxes; here the eight chunks
 // are the eight waves of one workgroup and the hand-offs go through LDS).
-// Grids of at most one unit a CU use 16 waves of 8 rows instead.
+// One-token calls and grids of at most one unit a CU use 16 waves of 8 rows.
 //
 // Lane layout of the state: lane l of wave w holds rows 16w + (l >> 3) and
 // 16w + 8 + (l >> 3) (16 waves: row 8w + (l >> 3)), columns 32m + 4(l & 7) ..
@@ -430,18 +430,26 @@ __global__ void kda_prepare_kernel(const PrepareParams in, const PreparedWeights
     }
 }
 
-// Up to one unit a CU, a unit's eight 16-row waves leave its per-token
-// arithmetic exposed between store bursts; sixteen 8-row waves halve each
-// wave's chain. Larger grids keep 2 eight-wave units a CU resident.
+// Waves a unit (measured on MI355X, same box, alternating runs): sixteen 8-row
+// waves for every one-token call (in-place decode: 73.8 against 77.5 us for
+// 256 requests x 12 heads, 21.4 against 22.6 for 64, although only one such
+// workgroup fits a CU) and for grids of at most one unit a CU, where a unit's
+// per-token arithmetic would otherwise sit exposed between its store bursts
+// (verify 16 x 4: 12.4 against 13.2 us); eight 16-row waves, two units a CU,
+// for larger multi-token grids (verify 64 x 8: 78.3 against 78.9 us).
 constexpr int64_t kSmallGrid = 256;   // MI355X compute units
 
 template <int L>
 hipError_t launch_core_t(const CoreParams& p, hipStream_t s) {
     const dim3 grid((unsigned)(p.requests * p.heads));
-    if ((int64_t)p.requests * p.heads <= kSmallGrid)
-        hipLaunchKernelGGL((kda_core_kernel<L, 16>), grid, dim3(1024), 0, s, p);
-    else
-        hipLaunchKernelGGL((kda_core_kernel<L, 8>), grid, dim3(512), 0, s, p);
+    if constexpr (L == 1) {
+        hipLaunchKernelGGL((kda_core_kernel<1, 16>), grid, dim3(1024), 0, s, p);
+    } else {
+        if ((int64_t)p.requests * p.heads <= kSmallGrid)
+            hipLaunchKernelGGL((kda_core_kernel<L, 16>), grid, dim3(1024), 0, s, p);
+        else
+            hipLaunchKernelGGL((kda_core_kernel<L, 8>), grid, dim3(512), 0, s, p);
+    }
     return hipGetLastError();
 }
 
