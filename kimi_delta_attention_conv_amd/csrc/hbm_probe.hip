@@ -127,14 +127,14 @@ __global__ __launch_bounds__(64 * WAVES) void probe_state_stream(float* __restri
     }
 }
 
-// The core kernel's choice of waves a unit: 16 for one token or at most 256
-// units, else 8.
+// The core kernel's choice of waves a unit: 16 for one token or at most one
+// unit a compute unit, else 8.
 template <int L>
 void launch_state_stream(float* state, int64_t slot_stride, int num_slots, const int32_t* slots,
                          int64_t row_stride, const int32_t* accepted, int requests, int heads,
-                         hipStream_t s) {
+                         int cu_count, hipStream_t s) {
     const dim3 grid((unsigned)(requests * heads));
-    if (L == 1 || (int64_t)requests * heads <= 256)
+    if (L == 1 || (int64_t)requests * heads <= cu_count)
         hipLaunchKernelGGL((probe_state_stream<L, 16>), grid, dim3(1024), 0, s, state, slot_stride,
                            num_slots, slots, row_stride, accepted, requests, heads);
     else
@@ -207,14 +207,18 @@ int kda_probe_state_stream(float* state, int64_t state_slot_stride, int32_t num_
         (reinterpret_cast<uintptr_t>(slots) & 3) != 0 ||
         (reinterpret_cast<uintptr_t>(accepted) & 3) != 0)
         return KDA_ERR_ALIGN;
+    int device = 0, cus = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess) return KDA_ERR_HIP;
     using Launch = void (*)(float*, int64_t, int, const int32_t*, int64_t, const int32_t*, int,
-                            int, hipStream_t);
+                            int, int, hipStream_t);
     static const Launch kLaunch[8] = {launch_state_stream<1>, launch_state_stream<2>,
                                       launch_state_stream<3>, launch_state_stream<4>,
                                       launch_state_stream<5>, launch_state_stream<6>,
                                       launch_state_stream<7>, launch_state_stream<8>};
     kLaunch[tokens - 1](state, state_slot_stride, num_slots, slots, slots_row_stride, accepted,
-                        requests, heads, static_cast<hipStream_t>(hip_stream));
+                        requests, heads, cus, static_cast<hipStream_t>(hip_stream));
     return launched();
 }
 

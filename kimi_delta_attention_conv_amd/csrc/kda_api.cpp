@@ -19,6 +19,7 @@
 
 struct kda_handle_s {
     int device = 0;
+    int32_t cu_count = 0;        // compute units of `device` (the core's choice of waves a unit)
     int32_t heads = 0;
     void* dev_mem = nullptr;
     kda::PreparedWeights w{};
@@ -98,6 +99,7 @@ kda::CoreParams core_params(const kda_handle_s* h, const void* projected, int64_
     p.norm_eps = h->norm_eps;
     p.l2_eps = h->l2_eps;
     p.handoff_bf16 = h->rounding == KDA_ROUND_BF16_HANDOFF;
+    p.cu_count = h->cu_count;
     // the dim-first pool [slots][3D][3] with 16-byte aligned slots takes the
     // kernel's coalesced window stores (each head's q, k, v windows are three
     // contiguous 768-byte runs whose starts are multiples of 16 bytes)
@@ -167,6 +169,13 @@ kda_status kda_prepare(const kda_weights* w, const kda_caches* c, void* hip_stre
         delete h;
         return hip_fail(e, "hipGetDevice");
     }
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device);
+    if (e != hipSuccess) {
+        delete h;
+        return hip_fail(e, "hipDeviceGetAttribute");
+    }
+    h->cu_count = cus;
     const int64_t b_conv_w = align_up(C * kda::kWidth * 4), b_conv_b = align_up(C * 4),
                   b_fb = align_up(D * kda::kFaRank * 2), b_a = align_up(H * 4),
                   b_dt = align_up(D * 4), b_nw = align_up(H * kda::kHeadDim * 4),

@@ -437,16 +437,16 @@ __global__ void kda_prepare_kernel(const PrepareParams in, const PreparedWeights
 // workgroup fits a CU) and for grids of at most one unit a CU, where a unit's
 // per-token arithmetic would otherwise sit exposed between its store bursts
 // (verify 16 x 4: 12.4 against 13.2 us); eight 16-row waves, two units a CU,
-// for larger multi-token grids (verify 64 x 8: 78.3 against 78.9 us).
-constexpr int64_t kSmallGrid = 256;   // MI355X compute units
-
+// for larger multi-token grids (verify 64 x 8: 78.3 against 78.9 us). "One
+// unit a CU" counts the device's compute units (256 on a whole MI355X, fewer
+// on a partition of one).
 template <int L>
 hipError_t launch_core_t(const CoreParams& p, hipStream_t s) {
     const dim3 grid((unsigned)(p.requests * p.heads));
     if constexpr (L == 1) {
         hipLaunchKernelGGL((kda_core_kernel<1, 16>), grid, dim3(1024), 0, s, p);
     } else {
-        if ((int64_t)p.requests * p.heads <= kSmallGrid)
+        if ((int64_t)p.requests * p.heads <= p.cu_count)
             hipLaunchKernelGGL((kda_core_kernel<L, 16>), grid, dim3(1024), 0, s, p);
         else
             hipLaunchKernelGGL((kda_core_kernel<L, 8>), grid, dim3(512), 0, s, p);

@@ -50,6 +50,7 @@ struct CoreParams {
     float l2_eps;
     int32_t conv_dim_first16;   // conv pool is dim first [slots][3D][3], 16-byte aligned
     int32_t handoff_bf16;       // round conv out, g1 and o to bf16 where produced
+    int32_t cu_count;           // compute units of the device (host side: waves a unit)
 };
 
 // Raw inputs of the weight re-layout kernel (device pointers).
