@@ -289,3 +289,31 @@ def test_bf16_small_weights_equal_fp32_bit_exact():
     for key in ("out", "conv", "state"):
         assert np.array_equal(f32[key], b16[key]), key
     assert_parity(rounded, run_oracle(rounded), b16, rounded.state.numpy(), label="bf16 small weights")
+
+
+@pytest.mark.parametrize("L", [2, 4])
+def test_eight_and_sixteen_wave_units_agree_bit_exact(L):
+    """The kernel runs a unit with 16 waves of 8 state rows for one-token calls and
+    for grids of at most one unit a compute unit, else with 8 waves of 16 rows; the
+    per-row arithmetic is the same in both. Requests are independent, so one verify
+    call over 32 requests x 12 heads (384 units: 8 waves on a 256-CU MI355X) and the
+    same requests as two calls of 16 (192 units each: 16 waves) must agree bit for
+    bit."""
+    from gpu_cases import GpuCase
+    print(f"[case] wave shapes L={L}", flush=True)
+    R = 32
+    case = make_case(R=R, L=L, H=12, num_slots=128, seed=430 + L, verify=True)
+    whole = GpuCase(case).run().host()
+    g = GpuCase(case)
+    half = R // 2
+    slots = g.case.slots.cuda()
+    acc = torch.as_tensor(case.accepted, dtype=torch.int32).cuda()
+    for k in range(2):
+        rows = slice(k * half * L, (k + 1) * half * L)
+        g.core.verify(g.projected[rows], g.out[rows], slots[k * half:(k + 1) * half],
+                      acc[k * half:(k + 1) * half])
+    torch.cuda.synchronize()
+    split = g.host()
+    for key in ("out", "conv", "state"):
+        assert np.array_equal(whole[key].view(np.uint8), split[key].view(np.uint8)), key
+    assert whole["errors"] == split["errors"] == 0
