@@ -37,11 +37,14 @@ def _expected(pool, table, accepted, tokens, valid):
     return out
 
 
-@pytest.mark.parametrize("tokens,verify", [(3, True), (8, True), (1, False)])
-def test_state_stream_probe_writes_scaled_carried_tiles(tokens, verify):
-    print(f"[case] state stream probe tokens={tokens} verify={verify}", flush=True)
+# (tokens, verify, requests, heads): 15-unit grids take the probe's 16-wave form,
+# 32 x 12 = 384 units with two tokens its 8-wave form (on a 256-CU device)
+@pytest.mark.parametrize("tokens,verify,R,H", [(3, True, 5, 3), (8, True, 5, 3), (1, False, 5, 3),
+                                               (2, True, 32, 12)])
+def test_state_stream_probe_writes_scaled_carried_tiles(tokens, verify, R, H):
+    print(f"[case] state stream probe tokens={tokens} verify={verify} R={R} H={H}", flush=True)
     lib = kda.load_library()
-    H, num_slots, R, cols = 3, 64, 5, 8 if tokens == 8 else 4
+    num_slots, cols = (64, 8 if tokens == 8 else 4) if R * 4 <= 64 else (160, 4)
     g = torch.Generator().manual_seed(900 + tokens)
     pool = torch.randn(num_slots, H, TILE, generator=g).numpy().astype(np.float32)
     perm = torch.randperm(num_slots, generator=g).numpy().astype(np.int32)
