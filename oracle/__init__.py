@@ -39,9 +39,7 @@ class Problem(ctypes.Structure):
         ("gate_lower_bound", ctypes.c_double), ("q_scale", ctypes.c_double),
         ("norm_eps", ctypes.c_double), ("l2_eps", ctypes.c_double),
         ("core_out", ctypes.c_void_p), ("core_out_f64", ctypes.c_void_p),
-        ("handoff_bf16", ctypes.c_int32), ("ties", ctypes.c_void_p),
-        ("tie_conv", ctypes.c_double), ("tie_g1", ctypes.c_double),
-        ("tie_o", ctypes.c_double), ("tie_y", ctypes.c_double),
+        ("handoff_bf16", ctypes.c_int32), ("check_distinct", ctypes.c_int32),
     ]
 
 
@@ -91,6 +89,8 @@ class Oracle:
         lib.kda_ref_gated_rmsnorm.restype = None
         lib.kda_ref_run.argtypes = [ctypes.POINTER(Problem)]
         lib.kda_ref_run.restype = i32
+        lib.kda_ref_handoff_ties.argtypes = [ctypes.POINTER(Problem), p, p]
+        lib.kda_ref_handoff_ties.restype = i32
         i64 = ctypes.c_int64
         lib.kda_ref_linear.argtypes = [i32, i32, i32, p, i64, p, p, i64, p]
         lib.kda_ref_linear.restype = None
@@ -190,17 +190,22 @@ class Oracle:
             accepted, num_slots, conv, conv_strides, state, state_slot_stride, conv_weight,
             conv_bias, f_b, A_log, dt_bias, norm_weight, norm_head_stride, gate_lower_bound,
             norm_eps, l2_eps, core_out, q_scale=HEAD_DIM ** -0.5, core_out_f64=None,
-            handoff_bf16=False, ties=None, tie_margins=(0.0, 0.0, 0.0, 0.0)) -> int:
+            handoff_bf16=False, check_distinct=False, ties=None,
+            tie_margins=(0.0, 0.0, 0.0, 0.0)) -> int:
         """One decode (accepted=None) or verify call, in place on host arrays.
 
         bf16 arrays are uint16 bit patterns. `conv`, `state` (whole pools) and
         `core_out` must be C-contiguous numpy arrays; they are updated in
         place. Returns the number of skipped requests.
 
-        handoff_bf16 rounds conv out, g1 and o to bf16 where produced. `ties`,
+        handoff_bf16 rounds conv out, g1 and o to bf16 where produced. A slot
+        named as a destination twice makes the call undefined (ValueError,
+        nothing written) unless check_distinct, which skips and counts every
+        request involved. `ties` (checker instrumentation, hand-off mode only),
         an int32 array [R, H, 4] zeroed by the caller, receives per (request,
         head) the near-tie counts of conv out, g1, o and core_out under the
-        relative margins `tie_margins` (conv, g1, o, core_out)."""
+        relative margins `tie_margins` (conv, g1, o, core_out); they are
+        counted by a separate read-only replay before the call runs."""
         projected = _u16(projected)
         slots = np.ascontiguousarray(np.asarray(slots, dtype=np.int32))
         acc = None if accepted is None else np.ascontiguousarray(
@@ -232,8 +237,13 @@ class Oracle:
             norm_head_stride=norm_head_stride, gate_lower_bound=gate_lower_bound,
             q_scale=q_scale, norm_eps=norm_eps, l2_eps=l2_eps, core_out=_ptr(core_out),
             core_out_f64=_ptr(core_out_f64), handoff_bf16=int(bool(handoff_bf16)),
-            ties=_ptr(ties), tie_conv=float(tie_margins[0]), tie_g1=float(tie_margins[1]),
-            tie_o=float(tie_margins[2]), tie_y=float(tie_margins[3]))
+            check_distinct=int(bool(check_distinct)))
+        if ties is not None:
+            assert handoff_bf16, "near ties are counted for the hand-off mode"
+            rel = np.ascontiguousarray(np.asarray(tie_margins, dtype=np.float64))
+            assert rel.size == 4
+            if self.lib.kda_ref_handoff_ties(ctypes.byref(pr), _ptr(rel), _ptr(ties)) < 0:
+                raise ValueError("oracle rejected the problem description")
         rc = self.lib.kda_ref_run(ctypes.byref(pr))
         if rc < 0:
             raise ValueError("oracle rejected the problem description")

@@ -25,32 +25,27 @@
  * for bit.
  *
  * Two rounding modes. Fused (handoff_bf16 = 0): nothing else is rounded.
- * Hand-off (handoff_bf16 = 1): the values an unfused pipeline passes between
- * its kernels as bf16 are rounded to bf16 (RNE) where they are produced --
- * the conv + SiLU outputs q|k|v, g1 = f_b f_a, and the recurrence output o --
- * which is the [kda] page's rounding rule (module docstring: elementwise
- * rounding follows the original path at every bf16 hand-off between the
- * original kernels).
+ * Hand-off (handoff_bf16 = 1): three values that an unfused stack of kernels
+ * would pass to the next kernel as bf16 tensors are rounded to bf16 (RNE)
+ * where they are produced -- the conv + SiLU outputs q|k|v, g1 = f_b f_a, and
+ * the recurrence output o ([kda] module docstring, the sentence on rounding:
+ * the fused kernels round as the unfused ones did wherever those exchanged
+ * bf16 data).
  *
- * Near-tie counters (hand-off checks). Another implementation computes each
- * rounded value in its own precision, so its rounding can differ from this
- * one's where the value lies close to a bf16 rounding boundary. Given a
- * caller's margin m for a value x (a bound on that implementation's error in
- * x), x counts as a near tie when x - m and x + m round to different bf16
- * values. Margins are relative factors times a magnitude: for a conv output
- * y = SiLU(pre), |SiLU'(pre)| (|bias| + sum |w * input|) + (1 + |pre|) |y| (the
- * pre-activation's rounding scaled by the slope, plus SiLU's own evaluation,
- * whose exponential sees an argument rounded relative to |pre|); for g1
- * sum |f_b f_a| (zero when every term is a
- * multiple of one quantum Q and the sum of |terms| is at most 2^24 Q, where
- * any fp32 summation order is exact); for o the sum over i of |S_dec q_i|
- * plus |beta| (|v| + sum |S_dec k_i|) sum |k_i q_i| (S_dec: the decayed
- * state row); for the core_out value its own magnitude.
+ * Destination slots. Each (request, token) of a call writes its own slot; a
+ * slot named twice in one call has no defined result, so such a call is
+ * rejected, or, when the problem asks for it (check_distinct), every request
+ * involved is skipped and counted like a request with an invalid index.
+ *
+ * kda_ref_run is the definition. kda_ref_handoff_ties, further down, is
+ * checker instrumentation for the hand-off mode's parity bars: it replays a
+ * call read-only and counts values that lie near a bf16 rounding boundary.
  *
  * Parity status: every step has a pin in the CPU tests (closed forms,
- * invariants, library routines, brute force). Readings that no printed value
- * fixes -- the l2norm epsilon, the norm-weight shape -- are the adopted
- * readings, not pinned by the pages.
+ * invariants, library routines, brute force). Parity unpinned: three readings
+ * that no printed value fixes -- the l2norm epsilon (1e-6 inside the square
+ * root), the norm weight shared by all heads, and which three values the
+ * hand-off mode rounds -- rest on this build's reading of the pages alone.
  */
 #include <math.h>
 #include <stdint.h>
@@ -157,7 +152,8 @@ void kda_ref_gate(int32_t H, const double* f_b, const double* f_a, const double*
 /* l2 normalisation with the epsilon inside the square root, then a scale
  * ([kda] kda tasks: "l2norm"; the 128^-0.5 q scale is the second of the
  * scalars in [prepared] PreparedKda.__init__):
- *   out = x * scale / sqrt(sum x^2 + eps). A zero vector maps to zero. */
+ *   out = x * scale / sqrt(sum x^2 + eps). With eps > 0 a zero vector maps to
+ * zero (the GPU library rejects eps <= 0). */
 void kda_ref_l2norm(int32_t n, const double* x, double eps, double scale, double* out)
 {
     double ss = 0.0;
@@ -239,11 +235,210 @@ typedef struct {
     uint16_t* core_out;         /* bf16 [S][D] */
     double* core_out_f64;       /* optional [S][D]: the value before the bf16 rounding */
     int32_t handoff_bf16;       /* 0 fused; 1 bf16 hand-offs (conv out, g1, o) */
-    int32_t* ties;              /* optional [R][H][4]: near ties of conv out, g1, o, core_out */
-    double tie_conv, tie_g1, tie_o, tie_y;   /* relative margins (see the header) */
+    int32_t check_distinct;     /* 0: a repeated destination makes the call undefined (-1);
+                                   1: requests with a repeated destination are skipped */
 } kda_ref_problem;
 
-/* bf16 rounding of x could go either way within +-m. */
+/* Slot resolution ([prepared] PreparedKda.run and _operands: slots [B] for a
+ * decode step; slots [>= B, q] with accepted [>= B] for a verify step).
+ * Decode: the state is read and written in place at slots[r]. Verify: the
+ * carried state is the one written for the last accepted token of the
+ * previous step, slots[r][accepted[r] - 1]; token t writes slots[r][t].
+ * Returns 0 when every index is in range, else -1 (the request is skipped). */
+static int resolve_slots(const kda_ref_problem* p, int32_t r, int32_t* src, int32_t* dst)
+{
+    const int32_t L = p->tokens;
+    const int32_t* row = p->slots + (int64_t)r * p->slots_row_stride;
+    for (int32_t t = 0; t < L; ++t) {
+        dst[t] = row[t];
+        if (dst[t] < 0 || dst[t] >= p->num_slots) return -1;
+    }
+    if (p->accepted == NULL) {
+        *src = dst[0];
+    } else {
+        int32_t a = p->accepted[r];
+        if (a < 1 || a > L) return -1;
+        *src = row[a - 1];
+    }
+    return 0;
+}
+
+/* Destination collisions. A call writes one state and one conv window per
+ * (request, token) to the slot the slots operand names; the pages give each
+ * token of each request its own slot ([prepared] run: a block-table slice of
+ * distinct cache lines), and a slot named twice in one call would receive two
+ * writes with no order between them. collide[r] is set for every request
+ * whose indices are all valid and one of whose destination slots is named
+ * more than once by such requests (twice in its own row included). Returns
+ * how many requests collide, or -1 when out of memory. */
+static int32_t find_collisions(const kda_ref_problem* p, int32_t* collide)
+{
+    const int32_t R = p->requests, L = p->tokens;
+    int32_t* count = calloc((size_t)p->num_slots, sizeof(int32_t));
+    int32_t* dst = malloc(sizeof(int32_t) * (size_t)L);
+    if (count == NULL || dst == NULL) { free(count); free(dst); return -1; }
+    int32_t src;
+    for (int32_t r = 0; r < R; ++r)
+        if (resolve_slots(p, r, &src, dst) == 0)
+            for (int32_t t = 0; t < L; ++t) ++count[dst[t]];
+    int32_t n = 0;
+    for (int32_t r = 0; r < R; ++r) {
+        collide[r] = 0;
+        if (resolve_slots(p, r, &src, dst) != 0) continue;
+        for (int32_t t = 0; t < L; ++t)
+            if (count[dst[t]] > 1) collide[r] = 1;
+        n += collide[r];
+    }
+    free(count);
+    free(dst);
+    return n;
+}
+
+/* The whole-problem checks kda_ref_run and kda_ref_handoff_ties share. */
+static int problem_ok(const kda_ref_problem* p)
+{
+    const int32_t H = p->heads, W = p->width, R = p->requests, L = p->tokens;
+    if (H <= 0 || W < 1 || R < 0 || L < 1 || p->pitch < 0 || p->num_slots < 0) return 0;
+    if (p->accepted == NULL && L != 1) return 0;
+    return p->pitch >= 4 * (int64_t)H * KDA_REF_HEAD_DIM + KDA_REF_FA_RANK + H;
+}
+
+/* Runs one call. The conv and state pools are updated in place; core_out rows
+ * of skipped requests are left untouched. Returns the number of skipped
+ * requests (an index out of range, or with check_distinct a repeated
+ * destination), or -1 on an invalid problem -- a repeated destination
+ * without check_distinct included, in which case nothing is written. */
+int32_t kda_ref_run(const kda_ref_problem* p)
+{
+    if (!problem_ok(p)) return -1;
+    const int32_t H = p->heads, W = p->width, R = p->requests, L = p->tokens;
+    const int32_t N = KDA_REF_HEAD_DIM, D = H * N, C = 3 * D;
+
+    int32_t* collide = malloc(sizeof(int32_t) * (size_t)(R > 0 ? R : 1));
+    if (collide == NULL) return -1;
+    const int32_t n_collide = find_collisions(p, collide);
+    if (n_collide < 0 || (n_collide > 0 && !p->check_distinct)) {
+        free(collide);
+        return -1;
+    }
+
+    /* Weights in double, nn.Conv1d weight [C][1][W] read as [C][W]. */
+    double* w = malloc(sizeof(double) * (size_t)C * W);
+    double* b = p->conv_bias ? malloc(sizeof(double) * (size_t)C) : NULL;
+    double* fb = malloc(sizeof(double) * (size_t)D * KDA_REF_FA_RANK);
+    double* alog = malloc(sizeof(double) * (size_t)H);
+    double* dtb = malloc(sizeof(double) * (size_t)D);
+    double* nw = malloc(sizeof(double) * (size_t)H * N);
+    double* win = malloc(sizeof(double) * (size_t)C * (W > 1 ? W - 1 : 1));
+    double* S = malloc(sizeof(double) * (size_t)H * N * N);
+    double* x = malloc(sizeof(double) * (size_t)p->pitch);
+    double* y = malloc(sizeof(double) * (size_t)C);
+    double* g = malloc(sizeof(double) * (size_t)D);
+    double* qh = malloc(sizeof(double) * (size_t)N);
+    double* kh = malloc(sizeof(double) * (size_t)N);
+    double* o = malloc(sizeof(double) * (size_t)N);
+    double* gate = malloc(sizeof(double) * (size_t)N);
+    double* yo = malloc(sizeof(double) * (size_t)N);
+    int32_t* dst = malloc(sizeof(int32_t) * (size_t)L);
+    const int hand = p->handoff_bf16 != 0;
+    for (int64_t i = 0; i < (int64_t)C * W; ++i) w[i] = kda_ref_bf16_to_double(p->conv_weight[i]);
+    if (b)
+        for (int32_t c = 0; c < C; ++c) b[c] = kda_ref_bf16_to_double(p->conv_bias[c]);
+    for (int64_t i = 0; i < (int64_t)D * KDA_REF_FA_RANK; ++i) fb[i] = kda_ref_bf16_to_double(p->f_b[i]);
+    for (int32_t h = 0; h < H; ++h) alog[h] = (double)p->A_log[h];
+    for (int32_t i = 0; i < D; ++i) dtb[i] = (double)p->dt_bias[i];
+    for (int32_t h = 0; h < H; ++h)
+        for (int32_t j = 0; j < N; ++j)
+            nw[(int64_t)h * N + j] = (double)p->norm_weight[(int64_t)h * p->norm_head_stride + j];
+
+    int32_t skipped = 0;
+    for (int32_t r = 0; r < R; ++r) {
+        int32_t src;
+        if (resolve_slots(p, r, &src, dst) != 0 || collide[r]) { ++skipped; continue; }
+
+        /* Read the carried conv window and state before any write. */
+        for (int32_t c = 0; c < C; ++c)
+            for (int32_t m = 0; m < W - 1; ++m)
+                win[(int64_t)c * (W - 1) + m] = kda_ref_bf16_to_double(
+                    p->conv[src * p->conv_slot_stride + c * p->conv_dim_stride + m * p->conv_pos_stride]);
+        for (int64_t e = 0; e < (int64_t)H * N * N; ++e)
+            S[e] = (double)p->state[src * p->state_slot_stride + e];
+
+        for (int32_t t = 0; t < L; ++t) {
+            const int64_t row = (int64_t)r * L + t;
+            const uint16_t* xr = p->projected + row * p->pitch;
+            for (int64_t e = 0; e < p->pitch; ++e) x[e] = kda_ref_bf16_to_double(xr[e]);
+
+            /* conv update + SiLU over q|k|v; the new window goes to dst[t] */
+            kda_ref_conv_token(C, W, w, b, win, x, y);
+            if (hand)
+                for (int32_t c = 0; c < C; ++c)
+                    y[c] = kda_ref_bf16_to_double(kda_ref_double_to_bf16(y[c]));   /* hand-off */
+            for (int32_t c = 0; c < C; ++c)
+                for (int32_t m = 0; m < W - 1; ++m)
+                    p->conv[dst[t] * p->conv_slot_stride + c * p->conv_dim_stride + m * p->conv_pos_stride] =
+                        kda_ref_double_to_bf16(win[(int64_t)c * (W - 1) + m]);
+
+            /* decay gate from f_a = projected[4D : 4D + 128] */
+            kda_ref_gate(H, fb, x + 4 * (int64_t)D, alog, dtb, p->gate_lower_bound, hand, g);
+
+            for (int32_t h = 0; h < H; ++h) {
+                /* beta = sigmoid(projected[4D + 128 + h]), one per (token, head) */
+                double beta = kda_ref_sigmoid(x[4 * (int64_t)D + KDA_REF_FA_RANK + h]);
+                kda_ref_l2norm(N, y + (int64_t)h * N, p->l2_eps, p->q_scale, qh);
+                kda_ref_l2norm(N, y + D + (int64_t)h * N, p->l2_eps, 1.0, kh);
+                const double* v = y + 2 * (int64_t)D + (int64_t)h * N;
+                double* Sh = S + (int64_t)h * N * N;
+                kda_ref_recur_token(N, N, Sh, g + (int64_t)h * N, kh, qh, v, beta, o);
+                if (hand)
+                    for (int32_t j = 0; j < N; ++j)
+                        o[j] = kda_ref_bf16_to_double(kda_ref_double_to_bf16(o[j]));   /* hand-off */
+
+                /* the state written for this token, rounded to fp32 and carried */
+                float* out_state = p->state + dst[t] * p->state_slot_stride + (int64_t)h * N * N;
+                for (int64_t e = 0; e < (int64_t)N * N; ++e) {
+                    float f = (float)Sh[e];
+                    out_state[e] = f;
+                    Sh[e] = (double)f;
+                }
+
+                /* gated RMSNorm with gate = projected[3D + 128 h + j] */
+                for (int32_t j = 0; j < N; ++j) gate[j] = x[3 * (int64_t)D + (int64_t)h * N + j];
+                kda_ref_gated_rmsnorm(N, o, gate, nw + (int64_t)h * N, p->norm_eps, yo);
+                for (int32_t j = 0; j < N; ++j) {
+                    int64_t oi = row * D + (int64_t)h * N + j;
+                    p->core_out[oi] = kda_ref_double_to_bf16(yo[j]);
+                    if (p->core_out_f64) p->core_out_f64[oi] = yo[j];
+                }
+            }
+        }
+    }
+
+    free(w); free(b); free(fb); free(alog); free(dtb); free(nw); free(win); free(S); free(x);
+    free(y); free(g); free(qh); free(kh); free(o); free(gate); free(yo); free(dst); free(collide);
+    return skipped;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Near ties of the hand-off mode (checker instrumentation, not the method) */
+/* ---------------------------------------------------------------------- */
+
+/* Another implementation computes each value it rounds to bf16 in its own
+ * precision, so where the value lies close to a bf16 rounding boundary its
+ * rounding can differ from the oracle's. Given a margin m for a value x (a
+ * bound on that implementation's error in x), x counts as a near tie when
+ * x - m and x + m round to different bf16 values. Margins are a relative
+ * factor times a magnitude:
+ *   conv out y = SiLU(pre):  |SiLU'(pre)| (|bias| + sum |w * input|) + (1 + |pre|) |y|
+ *       (the pre-activation's rounding scaled by the slope, plus SiLU's own
+ *       evaluation, whose exponential sees an argument rounded relative to |pre|);
+ *   g1 = sum_m f_b[m] f_a[m]:  sum |f_b f_a|, or zero when every term is a
+ *       multiple of one quantum Q and the sum of |terms| is at most 2^24 Q
+ *       (then every fp32 summation order is exact);
+ *   o:  sum_i |S_dec q_i| + |beta| (|v| + sum_i |S_dec k_i|) sum_i |k_i q_i|,
+ *       S_dec the decayed state row;
+ *   core_out value y:  |y|. */
+
 static int near_tie(double x, double m)
 {
     return m > 0.0 && kda_ref_double_to_bf16(x - m) != kda_ref_double_to_bf16(x + m);
@@ -276,42 +471,27 @@ static double g1_margin(const double* fbrow, const double* fa, double rel)
     return rel * mag;
 }
 
-/* Slot resolution ([prepared] PreparedKda.run and _operands: slots [B] for a
- * decode step; slots [>= B, q] with accepted [>= B] for a verify step).
- * Decode: the state is read and written in place at slots[r]. Verify: the
- * carried state is the one written for the last accepted token of the
- * previous step, slots[r][accepted[r] - 1]; token t writes slots[r][t].
- * Returns 0 when every index is in range, else -1 (the request is skipped). */
-static int resolve_slots(const kda_ref_problem* p, int32_t r, int32_t* src, int32_t* dst)
+/* Counts, per (request, head), the near ties among the values that the
+ * hand-off mode rounds -- conv out, g1, o -- and among core_out, under the
+ * relative margins rel[0..3] (conv, g1, o, core_out). ties is [R][H][4],
+ * zeroed by the caller. The call is the one kda_ref_run(p) performs with
+ * handoff_bf16 = 1, replayed with the same step functions on private copies:
+ * the pools are only read, so this runs before kda_ref_run on the same
+ * problem. Returns what kda_ref_run would (skipped count, or -1). */
+int32_t kda_ref_handoff_ties(const kda_ref_problem* p, const double* rel, int32_t* ties)
 {
-    const int32_t L = p->tokens;
-    const int32_t* row = p->slots + (int64_t)r * p->slots_row_stride;
-    for (int32_t t = 0; t < L; ++t) {
-        dst[t] = row[t];
-        if (dst[t] < 0 || dst[t] >= p->num_slots) return -1;
-    }
-    if (p->accepted == NULL) {
-        *src = dst[0];
-    } else {
-        int32_t a = p->accepted[r];
-        if (a < 1 || a > L) return -1;
-        *src = row[a - 1];
-    }
-    return 0;
-}
-
-/* Runs one call. The conv and state pools are updated in place; core_out rows
- * of skipped requests are left untouched. Returns the number of skipped
- * requests (an index out of range), or -1 on an invalid problem. */
-int32_t kda_ref_run(const kda_ref_problem* p)
-{
+    if (!problem_ok(p)) return -1;
     const int32_t H = p->heads, W = p->width, R = p->requests, L = p->tokens;
-    if (H <= 0 || W < 1 || R < 0 || L < 1 || p->pitch < 0) return -1;
-    if (p->accepted == NULL && L != 1) return -1;
     const int32_t N = KDA_REF_HEAD_DIM, D = H * N, C = 3 * D;
-    if (p->pitch < 4 * (int64_t)D + KDA_REF_FA_RANK + H) return -1;
 
-    /* Weights in double, nn.Conv1d weight [C][1][W] read as [C][W]. */
+    int32_t* collide = malloc(sizeof(int32_t) * (size_t)(R > 0 ? R : 1));
+    if (collide == NULL) return -1;
+    const int32_t n_collide = find_collisions(p, collide);
+    if (n_collide < 0 || (n_collide > 0 && !p->check_distinct)) {
+        free(collide);
+        return -1;
+    }
+
     double* w = malloc(sizeof(double) * (size_t)C * W);
     double* b = p->conv_bias ? malloc(sizeof(double) * (size_t)C) : NULL;
     double* fb = malloc(sizeof(double) * (size_t)D * KDA_REF_FA_RANK);
@@ -331,7 +511,6 @@ int32_t kda_ref_run(const kda_ref_problem* p)
     double* cmag = malloc(sizeof(double) * (size_t)C);
     double* omag = malloc(sizeof(double) * (size_t)N);
     int32_t* dst = malloc(sizeof(int32_t) * (size_t)L);
-    const int hand = p->handoff_bf16 != 0;
     for (int64_t i = 0; i < (int64_t)C * W; ++i) w[i] = kda_ref_bf16_to_double(p->conv_weight[i]);
     if (b)
         for (int32_t c = 0; c < C; ++c) b[c] = kda_ref_bf16_to_double(p->conv_bias[c]);
@@ -345,9 +524,8 @@ int32_t kda_ref_run(const kda_ref_problem* p)
     int32_t skipped = 0;
     for (int32_t r = 0; r < R; ++r) {
         int32_t src;
-        if (resolve_slots(p, r, &src, dst) != 0) { ++skipped; continue; }
-
-        /* Read the carried conv window and state before any write. */
+        if (resolve_slots(p, r, &src, dst) != 0 || collide[r]) { ++skipped; continue; }
+        int32_t* tr = ties + (int64_t)r * H * 4;
         for (int32_t c = 0; c < C; ++c)
             for (int32_t m = 0; m < W - 1; ++m)
                 win[(int64_t)c * (W - 1) + m] = kda_ref_bf16_to_double(
@@ -360,100 +538,72 @@ int32_t kda_ref_run(const kda_ref_problem* p)
             const uint16_t* xr = p->projected + row * p->pitch;
             for (int64_t e = 0; e < p->pitch; ++e) x[e] = kda_ref_bf16_to_double(xr[e]);
 
-            /* conv update + SiLU over q|k|v; the new window goes to dst[t] */
-            if (p->ties && hand)
-                for (int32_t c = 0; c < C; ++c) {
-                    double mg = b ? fabs(b[c]) : 0.0, pre = b ? b[c] : 0.0;
-                    for (int32_t m = 0; m < W - 1; ++m) {
-                        const double t = w[(int64_t)c * W + m] * win[(int64_t)c * (W - 1) + m];
-                        mg += fabs(t);
-                        pre += t;
-                    }
-                    const double t = w[(int64_t)c * W + W - 1] * x[c];
-                    mg += fabs(t);
-                    pre += t;
-                    const double sg = kda_ref_sigmoid(pre);
-                    const double slope = sg * (1.0 + pre * (1.0 - sg));   /* SiLU'(pre) */
-                    cmag[c] = fabs(slope) * mg + (1.0 + fabs(pre)) * fabs(pre * sg);
+            /* conv out: margins from the window before this token's shift */
+            for (int32_t c = 0; c < C; ++c) {
+                double mg = b ? fabs(b[c]) : 0.0, pre = b ? b[c] : 0.0;
+                for (int32_t m = 0; m < W - 1; ++m) {
+                    const double term = w[(int64_t)c * W + m] * win[(int64_t)c * (W - 1) + m];
+                    mg += fabs(term);
+                    pre += term;
                 }
+                const double term = w[(int64_t)c * W + W - 1] * x[c];
+                mg += fabs(term);
+                pre += term;
+                const double sg = kda_ref_sigmoid(pre);
+                const double slope = sg * (1.0 + pre * (1.0 - sg));   /* SiLU'(pre) */
+                cmag[c] = fabs(slope) * mg + (1.0 + fabs(pre)) * fabs(pre * sg);
+            }
             kda_ref_conv_token(C, W, w, b, win, x, y);
-            if (hand)
-                for (int32_t c = 0; c < C; ++c) {
-                    if (p->ties && near_tie(y[c], p->tie_conv * cmag[c]))
-                        ++p->ties[((int64_t)r * H + (c % D) / N) * 4 + 0];
-                    y[c] = kda_ref_bf16_to_double(kda_ref_double_to_bf16(y[c]));   /* hand-off */
-                }
-            for (int32_t c = 0; c < C; ++c)
-                for (int32_t m = 0; m < W - 1; ++m)
-                    p->conv[dst[t] * p->conv_slot_stride + c * p->conv_dim_stride + m * p->conv_pos_stride] =
-                        kda_ref_double_to_bf16(win[(int64_t)c * (W - 1) + m]);
+            for (int32_t c = 0; c < C; ++c) {
+                if (near_tie(y[c], rel[0] * cmag[c])) ++tr[((c % D) / N) * 4 + 0];
+                y[c] = kda_ref_bf16_to_double(kda_ref_double_to_bf16(y[c]));
+            }
 
-            /* decay gate from f_a = projected[4D : 4D + 128] */
-            kda_ref_gate(H, fb, x + 4 * (int64_t)D, alog, dtb, p->gate_lower_bound, hand, g);
-            if (p->ties && hand)
-                for (int32_t i = 0; i < D; ++i) {
-                    const double* fbrow = fb + (int64_t)i * KDA_REF_FA_RANK;
-                    const double* fa = x + 4 * (int64_t)D;
-                    double g1 = 0.0;
-                    for (int32_t m = 0; m < KDA_REF_FA_RANK; ++m) g1 += fbrow[m] * fa[m];
-                    if (near_tie(g1, g1_margin(fbrow, fa, p->tie_g1)))
-                        ++p->ties[((int64_t)r * H + i / N) * 4 + 1];
-                }
+            /* g1 */
+            const double* fa = x + 4 * (int64_t)D;
+            for (int32_t i = 0; i < D; ++i) {
+                const double* fbrow = fb + (int64_t)i * KDA_REF_FA_RANK;
+                double g1 = 0.0;
+                for (int32_t m = 0; m < KDA_REF_FA_RANK; ++m) g1 += fbrow[m] * fa[m];
+                if (near_tie(g1, g1_margin(fbrow, fa, rel[1]))) ++tr[(i / N) * 4 + 1];
+            }
+            kda_ref_gate(H, fb, fa, alog, dtb, p->gate_lower_bound, 1, g);
 
             for (int32_t h = 0; h < H; ++h) {
-                /* beta = sigmoid(projected[4D + 128 + h]), one per (token, head) */
                 double beta = kda_ref_sigmoid(x[4 * (int64_t)D + KDA_REF_FA_RANK + h]);
                 kda_ref_l2norm(N, y + (int64_t)h * N, p->l2_eps, p->q_scale, qh);
                 kda_ref_l2norm(N, y + D + (int64_t)h * N, p->l2_eps, 1.0, kh);
                 const double* v = y + 2 * (int64_t)D + (int64_t)h * N;
                 double* Sh = S + (int64_t)h * N * N;
-                if (p->ties && hand) {
-                    const double* gh = g + (int64_t)h * N;
-                    double kq = 0.0;
-                    for (int32_t i = 0; i < N; ++i) kq += fabs(kh[i] * qh[i]);
-                    for (int32_t j = 0; j < N; ++j) {
-                        double aq = 0.0, ak = 0.0;
-                        for (int32_t i = 0; i < N; ++i) {
-                            const double sd = Sh[(int64_t)j * N + i] * exp(gh[i]);
-                            aq += fabs(sd * qh[i]);
-                            ak += fabs(sd * kh[i]);
-                        }
-                        omag[j] = aq + fabs(beta) * (fabs(v[j]) + ak) * kq;
+                const double* gh = g + (int64_t)h * N;
+                double kq = 0.0;
+                for (int32_t i = 0; i < N; ++i) kq += fabs(kh[i] * qh[i]);
+                for (int32_t j = 0; j < N; ++j) {
+                    double aq = 0.0, ak = 0.0;
+                    for (int32_t i = 0; i < N; ++i) {
+                        const double sd = Sh[(int64_t)j * N + i] * exp(gh[i]);
+                        aq += fabs(sd * qh[i]);
+                        ak += fabs(sd * kh[i]);
                     }
+                    omag[j] = aq + fabs(beta) * (fabs(v[j]) + ak) * kq;
                 }
-                kda_ref_recur_token(N, N, Sh, g + (int64_t)h * N, kh, qh, v, beta, o);
-                if (hand)
-                    for (int32_t j = 0; j < N; ++j) {
-                        if (p->ties && near_tie(o[j], p->tie_o * omag[j]))
-                            ++p->ties[((int64_t)r * H + h) * 4 + 2];
-                        o[j] = kda_ref_bf16_to_double(kda_ref_double_to_bf16(o[j]));   /* hand-off */
-                    }
-
-                /* the state written for this token, rounded to fp32 and carried */
-                float* out_state = p->state + dst[t] * p->state_slot_stride + (int64_t)h * N * N;
-                for (int64_t e = 0; e < (int64_t)N * N; ++e) {
-                    float f = (float)Sh[e];
-                    out_state[e] = f;
-                    Sh[e] = (double)f;
+                kda_ref_recur_token(N, N, Sh, gh, kh, qh, v, beta, o);
+                for (int32_t j = 0; j < N; ++j) {
+                    if (near_tie(o[j], rel[2] * omag[j])) ++tr[h * 4 + 2];
+                    o[j] = kda_ref_bf16_to_double(kda_ref_double_to_bf16(o[j]));
                 }
-
-                /* gated RMSNorm with gate = projected[3D + 128 h + j] */
+                for (int64_t e = 0; e < (int64_t)N * N; ++e) Sh[e] = (double)(float)Sh[e];
                 for (int32_t j = 0; j < N; ++j) gate[j] = x[3 * (int64_t)D + (int64_t)h * N + j];
                 kda_ref_gated_rmsnorm(N, o, gate, nw + (int64_t)h * N, p->norm_eps, yo);
-                for (int32_t j = 0; j < N; ++j) {
-                    int64_t oi = row * D + (int64_t)h * N + j;
-                    p->core_out[oi] = kda_ref_double_to_bf16(yo[j]);
-                    if (p->core_out_f64) p->core_out_f64[oi] = yo[j];
-                    if (p->ties && near_tie(yo[j], p->tie_y * fabs(yo[j])))
-                        ++p->ties[((int64_t)r * H + h) * 4 + 3];
-                }
+                for (int32_t j = 0; j < N; ++j)
+                    if (near_tie(yo[j], rel[3] * fabs(yo[j]))) ++tr[h * 4 + 3];
             }
         }
     }
 
     free(w); free(b); free(fb); free(alog); free(dtb); free(nw); free(win); free(S); free(x);
     free(y); free(g); free(qh); free(kh); free(o); free(gate); free(yo); free(cmag); free(omag);
-    free(dst);
+    free(dst); free(collide);
     return skipped;
 }
 

@@ -341,34 +341,37 @@ def check_call_conv_window_closed_form(orc):
 @pin
 def check_call_verify_equals_chained_decodes(orc):
     """verify over L tokens == L decode calls chained on one slot, bit for bit
-    (core_out rows and every per-token state and conv window)."""
-    case = _small_verify(24)
-    res = run_oracle(case, orc)
-    src, dst = _src_dst(case)
-    D = case.D
-    for r in range(case.R):
-        conv = bf16_np(case.conv_storage).copy()
-        state = case.state.numpy().copy()
-        tmp = dst[r][0]  # chain in place on one slot, seeded with the source
-        conv[tmp] = conv[src[r]]
-        state[tmp] = state[src[r]]
-        for t in range(case.L):
-            row = r * case.L + t
-            out = np.zeros((1, D), np.uint16)
-            orc.run(heads=case.H, width=case.W, requests=1, tokens=1,
-                    projected=bf16_np(case.projected[row:row + 1]), pitch=case.pitch,
-                    slots=np.array([tmp], np.int32), slots_row_stride=1, accepted=None,
-                    num_slots=case.num_slots, conv=conv.reshape(-1),
-                    conv_strides=case.conv_strides(), state=state.reshape(-1),
-                    state_slot_stride=case.H * 128 * 128, conv_weight=bf16_np(case.conv_weight),
-                    conv_bias=bf16_np(case.conv_bias), f_b=bf16_np(case.f_b),
-                    A_log=case.A_log.numpy(), dt_bias=case.dt_bias.numpy(),
-                    norm_weight=case.norm_weight.numpy(), norm_head_stride=0,
-                    gate_lower_bound=case.gate_lower_bound, norm_eps=case.norm_eps,
-                    l2_eps=case.l2_eps, core_out=out)
-            assert np.array_equal(out[0], res["out"][row]), (r, t)
-            assert np.array_equal(state[tmp], res["state"][dst[r][t]]), (r, t)
-            assert np.array_equal(conv[tmp], res["conv"][dst[r][t]]), (r, t)
+    (core_out rows and every per-token state and conv window), in the fused and
+    in the bf16 hand-off mode."""
+    for hand in (False, True):
+        case = _small_verify(24)
+        res = run_oracle(case, orc, handoff_bf16=hand)
+        src, dst = _src_dst(case)
+        D = case.D
+        for r in range(case.R):
+            conv = bf16_np(case.conv_storage).copy()
+            state = case.state.numpy().copy()
+            tmp = dst[r][0]  # chain in place on one slot, seeded with the source
+            conv[tmp] = conv[src[r]]
+            state[tmp] = state[src[r]]
+            for t in range(case.L):
+                row = r * case.L + t
+                out = np.zeros((1, D), np.uint16)
+                orc.run(heads=case.H, width=case.W, requests=1, tokens=1,
+                        projected=bf16_np(case.projected[row:row + 1]), pitch=case.pitch,
+                        slots=np.array([tmp], np.int32), slots_row_stride=1, accepted=None,
+                        num_slots=case.num_slots, conv=conv.reshape(-1),
+                        conv_strides=case.conv_strides(), state=state.reshape(-1),
+                        state_slot_stride=case.H * 128 * 128,
+                        conv_weight=bf16_np(case.conv_weight),
+                        conv_bias=bf16_np(case.conv_bias), f_b=bf16_np(case.f_b),
+                        A_log=case.A_log.numpy(), dt_bias=case.dt_bias.numpy(),
+                        norm_weight=case.norm_weight.numpy(), norm_head_stride=0,
+                        gate_lower_bound=case.gate_lower_bound, norm_eps=case.norm_eps,
+                        l2_eps=case.l2_eps, core_out=out, handoff_bf16=hand)
+                assert np.array_equal(out[0], res["out"][row]), (hand, r, t)
+                assert np.array_equal(state[tmp], res["state"][dst[r][t]]), (hand, r, t)
+                assert np.array_equal(conv[tmp], res["conv"][dst[r][t]]), (hand, r, t)
 
 
 @pin
@@ -439,6 +442,66 @@ def check_call_skips_invalid_requests(orc):
     for slot in range(case.num_slots):
         if slot not in written:
             assert np.array_equal(res["state"][slot], before[slot]), slot
+
+
+@pin
+def check_call_duplicate_destinations(orc):
+    """A slot named twice as a destination in one call -- by two requests, or by two
+    tokens of one request -- makes the call undefined: the oracle rejects it and
+    writes nothing. With check_distinct every request involved is skipped and
+    counted, and the others are as if run alone."""
+    base = make_case(R=4, L=3, H=2, num_slots=24, seed=34, verify=True)
+    for kind in ("across", "within"):
+        s = base.slots.clone()
+        if kind == "across":
+            s[2, 1] = s[0, 2]          # requests 0 and 2 share a destination
+            involved = {0, 2}
+        else:
+            s[1, 2] = s[1, 0]          # request 1 names one slot for tokens 0 and 2
+            involved = {1}
+        case = dataclasses.replace(base, slots=s)
+        conv = bf16_np(case.conv_storage)
+        state = case.state.numpy().copy()
+        out = np.zeros((case.S, case.D), np.uint16)
+        try:
+            run_oracle(case, orc)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError(f"duplicate destinations ({kind}) accepted")
+        # nothing written on rejection: run in place on explicit arrays
+        kw = dict(heads=case.H, width=case.W, requests=case.R, tokens=case.L,
+                  projected=bf16_np(case.projected), pitch=case.pitch,
+                  slots=s.contiguous().numpy(), slots_row_stride=case.L,
+                  accepted=case.accepted.numpy(), num_slots=case.num_slots,
+                  conv=conv.reshape(-1), conv_strides=case.conv_strides(),
+                  state=state.reshape(-1), state_slot_stride=case.H * 128 * 128,
+                  conv_weight=bf16_np(case.conv_weight), conv_bias=bf16_np(case.conv_bias),
+                  f_b=bf16_np(case.f_b), A_log=case.A_log.numpy(),
+                  dt_bias=case.dt_bias.numpy(), norm_weight=case.norm_weight.numpy(),
+                  norm_head_stride=0, gate_lower_bound=case.gate_lower_bound,
+                  norm_eps=case.norm_eps, l2_eps=case.l2_eps, core_out=out)
+        try:
+            orc.run(**kw)
+        except ValueError:
+            pass
+        assert np.array_equal(conv, bf16_np(case.conv_storage)) and \
+            np.array_equal(state, case.state.numpy()) and not out.any(), kind
+        res = run_oracle(case, orc, check_distinct=True)
+        assert res["skipped"] == len(involved), (kind, res["skipped"])
+        keep = [r for r in range(case.R) if r not in involved]
+        for r in involved:
+            assert not res["out"][r * case.L:(r + 1) * case.L].any(), (kind, r)
+        alone = dataclasses.replace(
+            case, R=len(keep),
+            projected=torch.cat([case.projected[r * case.L:(r + 1) * case.L] for r in keep]),
+            slots=s[keep].clone(), accepted=case.accepted[keep].clone())
+        ref = run_oracle(alone, orc)
+        for i, r in enumerate(keep):
+            assert np.array_equal(res["out"][r * case.L:(r + 1) * case.L],
+                                  ref["out"][i * case.L:(i + 1) * case.L]), (kind, r)
+        assert np.array_equal(res["state"], ref["state"]), kind
+        assert np.array_equal(res["conv"], ref["conv"]), kind
 
 
 @pin
@@ -634,3 +697,27 @@ def check_handoff_g1_tie_certificate(orc):
             sl = slice(128 * h, 128 * (h + 1))
             assert ties[r, h, 1] == _near_ties(g1[sl], mu * mag[sl]), (r, h)
     assert ties[:, :, 1].sum() > 0
+
+
+@pin
+def check_handoff_ties_replay_matches_run(orc):
+    """The near-tie counter replays the call on its own copies: its core_out values
+    must be the run's. Over a three-token verify, the core_out near ties it counts
+    per (request, head) equal a brute-force count over the run's unrounded core_out
+    at the same margin (2^-12 relative: about one value in eight counts), so a
+    replay that drifted from the run by more than a small fraction of that margin
+    in any step or token would disagree (an fp32-level drift, ~1e-8, would not)."""
+    case = _small_verify(35)
+    mu = 2.0 ** -12
+    ties = np.zeros((case.R, case.H, 4), np.int32)
+    res = run_oracle(case, orc, handoff_bf16=True, ties=ties, tie_margins=(0.0, 0.0, 0.0, mu))
+    y = res["out_f64"]
+    total = 0
+    for r in range(case.R):
+        rows = y[r * case.L:(r + 1) * case.L]
+        for h in range(case.H):
+            v = rows[:, 128 * h: 128 * (h + 1)]
+            n = _near_ties(v, mu * np.abs(v))
+            assert ties[r, h, 3] == n, (r, h, ties[r, h, 3], n)
+            total += n
+    assert total > 0.05 * y.size, total

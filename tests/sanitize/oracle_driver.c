@@ -1,5 +1,6 @@
-/* Drives the oracle through decode, verify (with skipped requests), the hand-off mode
- * with near-tie counters and the projection reference, on small pseudo-random inputs. */
+/* Drives the oracle through decode, verify (with skipped requests), repeated
+ * destinations (rejected, or skipped when checked), the hand-off mode with its
+ * near-tie replay and the projection reference, on small pseudo-random inputs. */
 #include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
@@ -20,7 +21,7 @@ static float* f_array(size_t n, double lo, double hi) {
 }
 
 static int run_case(int H, int R, int L, int verify, int dim_first, int with_bias, int per_head,
-                    int handoff, int bad_request) {
+                    int handoff, int bad_request, int dup, int check) {
     const int N = 128, D = H * N, C = 3 * D, W = 4, slots_n = R * L + 3;
     const int64_t pitch = 4 * (int64_t)D + 128 + H + 6, S = (int64_t)R * L;
     uint16_t* projected = bf_array((size_t)(S * pitch), 1.0);
@@ -37,6 +38,7 @@ static int run_case(int H, int R, int L, int verify, int dim_first, int with_bia
     int32_t* acc = malloc(sizeof(int32_t) * (size_t)R);
     for (int r = 0; r < R; ++r) acc[r] = 1 + r % L;
     if (bad_request) { if (verify) acc[0] = L + 1; else slots[0] = slots_n + 5; }
+    if (dup) slots[2 * (L + 1)] = slots[L + 1];   /* requests 1 and 2 share a destination */
     uint16_t* out = calloc((size_t)(S * D), sizeof *out);
     double* out64 = calloc((size_t)(S * D), sizeof *out64);
     int32_t* ties = calloc((size_t)R * H * 4, sizeof *ties);
@@ -55,21 +57,27 @@ static int run_case(int H, int R, int L, int verify, int dim_first, int with_bia
     p.norm_weight = nw; p.norm_head_stride = per_head ? N : 0;
     p.gate_lower_bound = -5.0; p.q_scale = 1.0 / sqrt(128.0); p.norm_eps = 1e-6; p.l2_eps = 1e-6;
     p.core_out = out; p.core_out_f64 = out64;
-    p.handoff_bf16 = handoff; p.ties = handoff ? ties : NULL;
-    p.tie_conv = p.tie_g1 = p.tie_o = p.tie_y = 1e-6;
+    p.handoff_bf16 = handoff; p.check_distinct = check;
+    const double rel[4] = {1e-6, 1e-6, 1e-6, 1e-6};
+    const int32_t expect = dup ? (check ? 2 + bad_request : -1) : bad_request;
+    int bad = 0;
+    if (handoff) bad |= kda_ref_handoff_ties(&p, rel, ties) != expect;
     const int32_t skipped = kda_ref_run(&p);
     free(projected); free(conv); free(state); free(cw); free(cb); free(fb); free(alog);
     free(dtb); free(nw); free(slots); free(acc); free(out); free(out64); free(ties);
-    return skipped == (bad_request ? 1 : 0) ? 0 : 1;
+    return bad || skipped != expect;
 }
 
 int main(void) {
     int bad = 0;
-    bad |= run_case(2, 3, 1, 0, 1, 1, 0, 0, 0);
-    bad |= run_case(2, 3, 1, 0, 0, 0, 1, 0, 1);
-    bad |= run_case(1, 2, 3, 1, 1, 1, 0, 0, 0);
-    bad |= run_case(3, 2, 8, 1, 0, 1, 1, 0, 1);
-    bad |= run_case(2, 2, 4, 1, 1, 1, 0, 1, 0);
+    bad |= run_case(2, 3, 1, 0, 1, 1, 0, 0, 0, 0, 0);
+    bad |= run_case(2, 3, 1, 0, 0, 0, 1, 0, 1, 0, 0);
+    bad |= run_case(1, 2, 3, 1, 1, 1, 0, 0, 0, 0, 0);
+    bad |= run_case(3, 2, 8, 1, 0, 1, 1, 0, 1, 0, 0);
+    bad |= run_case(2, 2, 4, 1, 1, 1, 0, 1, 0, 0, 0);
+    bad |= run_case(1, 4, 2, 1, 1, 1, 0, 1, 1, 1, 0);
+    bad |= run_case(1, 4, 2, 1, 0, 1, 0, 1, 1, 1, 1);
+    bad |= run_case(2, 3, 1, 0, 1, 0, 0, 0, 0, 1, 1);
     {   /* projection reference, with a padded x pitch */
         const int M = 5, Nn = 7, K = 24;
         uint16_t* x = bf_array((size_t)M * (K + 8), 1.0);

@@ -67,18 +67,45 @@ MUTATIONS = {
                                         "return 0.0;"),
     "tie_o_margin_drops_delta_term": ("omag[j] = aq + fabs(beta) * (fabs(v[j]) + ak) * kq;",
                                       "omag[j] = aq;"),
-    "tie_y_counted_on_wrong_head": ("++p->ties[((int64_t)r * H + h) * 4 + 3];",
-                                    "++p->ties[((int64_t)r * H + 0) * 4 + 3];"),
+    "tie_y_counted_on_wrong_head": ("++tr[h * 4 + 3];", "++tr[0 * 4 + 3];"),
+    "tie_replay_conv_not_rounded": (
+        "if (near_tie(y[c], rel[0] * cmag[c])) ++tr[((c % D) / N) * 4 + 0];\n"
+        "                y[c] = kda_ref_bf16_to_double(kda_ref_double_to_bf16(y[c]));",
+        "if (near_tie(y[c], rel[0] * cmag[c])) ++tr[((c % D) / N) * 4 + 0];"),
+    "duplicate_threshold_off_by_one": ("if (count[dst[t]] > 1) collide[r] = 1;",
+                                       "if (count[dst[t]] > 2) collide[r] = 1;"),
+    "duplicate_within_row_ignored": (
+        "for (int32_t t = 0; t < L; ++t) ++count[dst[t]];",
+        "for (int32_t t = 0; t < L; ++t) count[dst[t]] = count[dst[t]] < r + 1 ? r + 1 : count[dst[t]] + 1;"),
+    "duplicate_collider_not_skipped": (
+        "if (resolve_slots(p, r, &src, dst) != 0 || collide[r]) { ++skipped; continue; }\n\n"
+        "        /* Read the carried",
+        "if (resolve_slots(p, r, &src, dst) != 0) { ++skipped; continue; }\n\n"
+        "        /* Read the carried"),
 }
+
+
+# The near-tie replay (checker instrumentation) repeats some of the definition's
+# expressions; a mutation named tie_* is planted in the replay, any other in the
+# definition (everything before the replay's section).
+REPLAY_MARK = "/* Near ties of the hand-off mode"
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_planted_mistake_is_caught(name, tmp_path):
     old, new = MUTATIONS[name]
     src = open(SRC).read()
-    assert src.count(old) == 1, f"mutation anchor not unique in the oracle: {old!r}"
+    cut = src.index(REPLAY_MARK)
+    end = src.index("/* Projections around the core")
+    if name.startswith("tie_"):
+        head, region, tail = src[:cut], src[cut:end], src[end:]
+    elif name.startswith("linear_"):
+        head, region, tail = src[:end], src[end:], ""
+    else:
+        head, region, tail = "", src[:cut], src[cut:]
+    assert region.count(old) == 1, f"mutation anchor not unique in its region: {old!r}"
     mutated = tmp_path / "kda_oracle_mutant.c"
-    mutated.write_text(src.replace(old, new))
+    mutated.write_text(head + region.replace(old, new) + tail)
     lib = tmp_path / "libmutant.so"
     subprocess.run(["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
                     "-o", str(lib), str(mutated), "-lm"], check=True)
