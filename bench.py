@@ -8,7 +8,7 @@ seeded synthetic tensors at the pages' shapes (12 heads x 128 channels per
 tensor-parallel rank, f_a rank 128, width-4 conv), resident in HBM before the
 timed region starts.
 
-The default workload is the large spec-verify batch: R = 64 requests x L = 8
+The headline workload is the large spec-verify batch: R = 64 requests x L = 8
 tokens (S = 512 rows), a pool of 1024 slots addressed through a [64, 16] block
 table, accepted counts ~ U{1..8}. Successive steps alternate between the two
 8-column halves of the block table, so that a step's reads come from slots
@@ -19,16 +19,26 @@ Metric bytes per step (state + conv window, read once per request and written
 once per token): (R + S) x H x 67,840 B, where a unit of 67,840 B is one
 128 x 128 fp32 state tile plus one 3 x 384 bf16 conv window.
 
-Prints one JSON line. The default run also times the large decode batch
-(R = 256, L = 1, four disjoint slot sets rotating; kernel time only) and adds it
-under `decode_r256`. `--config N` selects another workload (0..4) for
-exploration; `--probe` adds the plain read / write / copy HBM probes.
+Prints one JSON line. Besides the headline it carries, under `configs`, every
+one of the five workloads (tiny decode, decode 64, verify 16 x 4, verify 64 x 8,
+decode 256): kernel time over back-to-back launches with slot sets rotating,
+tokens/s, metric GB/s and fraction of the HBM peak, the same kernel against the
+ceiling of its own access pattern (the fastest replay of its state traffic
+with no arithmetic, include/kda_probe.h; for decode also a plain device copy of
+the same bytes), and per-launch times. The pools of the three small workloads
+fit the 256 MB Infinity Cache, so for them the line adds a flushed figure: each
+launch timed alone after 1 GiB of other writes.
+
+`--trace-only` runs only the headline's rotated timed launches (for
+rocprofv3 kernel traces and counters); `--config N` picks the headline
+workload; `--layer` / `--proj` time the projections around the core.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -39,6 +49,7 @@ if ROOT not in sys.path:
 METRIC = "KDA verify tokens/s and achieved HBM GB/s (state+conv R/W) at R x L"
 UNIT_BYTES = 128 * 128 * 4 + 3 * 128 * 3 * 2        # state tile + conv window of one head
 HBM_PEAK_GBPS = 8000.0                                # MI355X published HBM3E bandwidth
+MALL_BYTES = 256 << 20                                # MI355X Infinity Cache
 KERNEL_NAME = "kda_core_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_core_traffic.json")
 
@@ -48,19 +59,19 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=3, help="workload 0..4 (default 3)")
+    ap.add_argument("--config", type=int, default=3, help="headline workload 0..4 (default 3)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the oracle baseline (0 disables it)")
     ap.add_argument("--rounding", choices=("fused", "bf16_handoff"), default="fused",
                     help="core rounding mode (default fused)")
-    ap.add_argument("--probe", action="store_true",
-                    help="run the HBM probes (the default; kept for older command lines)")
-    ap.add_argument("--no-probe", action="store_true", help="skip the HBM probes")
-    ap.add_argument("--skip-decode", action="store_true",
-                    help="with the default workload, skip the decode R=256 timing that the "
-                         "line also carries")
+    ap.add_argument("--no-probe", action="store_true", help="skip the plain HBM probes")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload table (headline only)")
+    ap.add_argument("--trace-only", action="store_true",
+                    help="run only the headline's warm-up and rotated timed launches (for "
+                         "rocprofv3 traces): no per-launch, pattern, probe, table or CPU legs")
     ap.add_argument("--probe-only", action="store_true",
-                    help="run only the HBM probes (counter calibration)")
+                    help="run only the plain HBM probes (counter calibration)")
     ap.add_argument("--graph", type=int, default=0, metavar="CHAIN",
                     help="capture CHAIN consecutive launches (rotating slot sets) in one HIP "
                          "graph and time graph replays (steps rounded up to whole replays)")
@@ -102,103 +113,179 @@ def rotation_sets(case, torch):
     return torch.cat(chunks).contiguous(), views
 
 
-def time_pattern(torch, lib, state, case, sets, accepted, steps, warmup):
-    """The core's state traffic alone (kda_probe_state_stream: same grid, slots,
-    tile loads and per-token stores, no arithmetic, no conv windows) over the
-    same rotating slot sets: the ceiling of the kernel's access pattern."""
-    stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
-    stride = case.H * 128 * 128
+class Workload:
+    """One workload's inputs on the device, its core handle and its launches."""
 
-    def launch(i):
-        s = sets[i % len(sets)]
-        return lib.kda_probe_state_stream(state.data_ptr(), stride, case.num_slots, s.data_ptr(),
-                                          s.stride(0) if s.dim() == 2 else 1,
-                                          None if accepted is None else accepted.data_ptr(),
-                                          case.R, case.L, case.H, sp)
+    def __init__(self, torch, kda, index, rounding="fused"):
+        from kda_inputs import make_config
 
+        self.torch = torch
+        self.case = case = make_config(index)
+        dev = "cuda"
+        self.conv_storage = case.conv_storage.to(dev)
+        conv = self.conv_storage if case.conv_dim_first else self.conv_storage.transpose(-1, -2)
+        self.state = case.state.to(dev)
+        self.core = kda.KdaCore(conv_weight=case.conv_weight.to(dev),
+                                conv_bias=None if case.conv_bias is None else case.conv_bias.to(dev),
+                                f_b=case.f_b.to(dev), A_log=case.A_log.to(dev),
+                                dt_bias=case.dt_bias.to(dev), norm_weight=case.norm_weight.to(dev),
+                                gate_lower_bound=case.gate_lower_bound, norm_eps=case.norm_eps,
+                                l2_eps=case.l2_eps, conv=conv, state=self.state, rounding=rounding)
+        self.projected = case.projected.to(dev)
+        self.out = torch.empty(case.S, case.D, dtype=torch.bfloat16, device=dev)
+        base, views = rotation_sets(case, torch)
+        self.slot_base = base.to(dev)
+        self.sets = [torch.as_strided(self.slot_base, sh, st, off) for sh, st, off in views]
+        self.accepted = None if case.accepted is None else case.accepted.to(dev)
+        self.lib = kda.load_library()
+        self.metric_bytes = (case.R + case.S) * case.H * UNIT_BYTES
+        # bytes of the slots one launch touches: the MALL holds them when small
+        self.pool_bytes = case.num_slots * case.H * UNIT_BYTES
+
+    def make_launch(self, s, sp):
+        lib, c, h = self.lib, self.case, self.core.handle
+        proj, out = self.projected.data_ptr(), self.out.data_ptr()
+        if self.accepted is None:
+            return lambda: lib.kda_decode(h, proj, c.pitch, c.R, s.data_ptr(), out, sp)
+        acc = self.accepted.data_ptr()
+        return lambda: lib.kda_verify(h, proj, c.pitch, c.R, c.L, s.data_ptr(), s.stride(0), acc,
+                                      out, sp)
+
+    def launches(self, sp):
+        return [self.make_launch(s, sp) for s in self.sets]
+
+    def check_errors(self):
+        n = self.core.device_errors()
+        if n:
+            raise RuntimeError(f"{self.case.name}: {n} requests were skipped for invalid slots")
+
+    def close(self):
+        self.core.close()
+
+
+def events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_back_to_back(torch, fns, steps, warmup, stream):
+    """Average ms of one call over `steps` back-to-back calls (rotating through
+    `fns`), HIP events on the launch stream."""
     for i in range(warmup):
-        if launch(i) != 0:
-            raise RuntimeError("state stream probe failed")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if fns[i % len(fns)]() != 0:
+            raise RuntimeError("launch failed")
     torch.cuda.synchronize()
+    e0, e1 = events(torch)
     e0.record(stream)
-    failed = sum(launch(warmup + i) != 0 for i in range(steps))
+    failed = sum(fns[(warmup + i) % len(fns)]() != 0 for i in range(steps))
     e1.record(stream)
     torch.cuda.synchronize()
     if failed:
-        raise RuntimeError(f"state stream probe: {failed} launches failed")
-    ms = e0.elapsed_time(e1) / steps
-    state_bytes = (case.R + case.S) * case.H * 128 * 128 * 4
-    return {"kernel_ms": round(ms, 5), "state_bytes": state_bytes,
-            "gbps": round(state_bytes / (ms * 1e-3) / 1e9, 1)}
+        raise RuntimeError(f"{failed} launches failed")
+    return e0.elapsed_time(e1) / steps
 
 
-def time_workload(torch, kda, index, steps, warmup):
-    """Kernel time of one more workload on the current stream (HIP events over
-    `steps` launches after `warmup`, slot sets rotating as in the main run);
-    returns its tokens/s, metric GB/s and fraction of the HBM peak."""
-    from kda_inputs import make_config
+def time_each(torch, fns, n, stream, before=None):
+    """Per-launch µs of `n` calls, each between its own pair of events, with
+    `before()` (e.g. a cache flush) enqueued ahead of each pair."""
+    pairs = []
+    for i in range(n):
+        if before is not None:
+            before()
+        a, b = events(torch)
+        a.record(stream)
+        if fns[i % len(fns)]() != 0:
+            raise RuntimeError("launch failed")
+        b.record(stream)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
+    q = lambda f: us[min(len(us) - 1, int(f * len(us)))]
+    return {"p10": round(q(0.1), 2), "p50": round(statistics.median(us), 2),
+            "p90": round(q(0.9), 2), "launches": n}
 
-    case = make_config(index)
-    dev = "cuda"
-    conv_storage = case.conv_storage.to(dev)
-    conv = conv_storage if case.conv_dim_first else conv_storage.transpose(-1, -2)
-    state = case.state.to(dev)
-    core = kda.KdaCore(conv_weight=case.conv_weight.to(dev),
-                       conv_bias=None if case.conv_bias is None else case.conv_bias.to(dev),
-                       f_b=case.f_b.to(dev), A_log=case.A_log.to(dev),
-                       dt_bias=case.dt_bias.to(dev), norm_weight=case.norm_weight.to(dev),
-                       gate_lower_bound=case.gate_lower_bound, norm_eps=case.norm_eps,
-                       l2_eps=case.l2_eps, conv=conv, state=state)
-    projected = case.projected.to(dev)
-    out = torch.empty(case.S, case.D, dtype=torch.bfloat16, device=dev)
-    slot_base, views = rotation_sets(case, torch)
-    slot_base = slot_base.to(dev)
-    sets = [torch.as_strided(slot_base, shape, stride, off) for shape, stride, off in views]
-    accepted = None if case.accepted is None else case.accepted.to(dev)
-    lib = kda.load_library()
-    stream = torch.cuda.current_stream()
+
+def pattern_ceiling(torch, w, steps, stream):
+    """The workload's state traffic alone (kda_probe_state_stream over the same
+    rotating slot sets) in each probe variant, and for in-place decode a device
+    copy of the same bytes; the fastest is the ceiling of the access pattern."""
+    from kimi_delta_attention_conv_amd import probe as kprobe
+    plib = kprobe.load_probe_library()
+    c = w.case
     sp = stream.cuda_stream
-
-    def launch(i):
-        s = sets[i % len(sets)]
-        if accepted is None:
-            return lib.kda_decode(core.handle, projected.data_ptr(), case.pitch, case.R,
-                                  s.data_ptr(), out.data_ptr(), sp)
-        return lib.kda_verify(core.handle, projected.data_ptr(), case.pitch, case.R, case.L,
-                              s.data_ptr(), s.stride(0), accepted.data_ptr(), out.data_ptr(), sp)
-
-    for i in range(warmup):
-        if launch(i) != 0:
-            raise RuntimeError(f"{case.name}: launch failed")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    failed = sum(launch(warmup + i) != 0 for i in range(steps))
-    e1.record(stream)
-    torch.cuda.synchronize()
-    if failed:
-        raise RuntimeError(f"{case.name}: {failed} launches failed")
-    if core.device_errors():
-        raise RuntimeError(f"{case.name}: requests were skipped for invalid slots")
-    kernel_ms = e0.elapsed_time(e1) / steps
-    metric_bytes = (case.R + case.S) * case.H * UNIT_BYTES
-    gbps = metric_bytes / (kernel_ms * 1e-3) / 1e9
-    core.close()
-    pattern = time_pattern(torch, lib, state, case, sets, accepted, steps, warmup)
-    return {"workload": case.name, "requests": case.R, "tokens": case.L,
-            "tokens_per_s": round(case.S / (kernel_ms * 1e-3), 1),
-            "kernel_ms": round(kernel_ms, 5), "gbps": round(gbps, 1),
-            "frac": round(gbps / HBM_PEAK_GBPS, 4), "metric_bytes_per_step": metric_bytes,
-            "pattern_probe": pattern,
-            "frac_of_pattern": round(pattern["kernel_ms"] / kernel_ms, 4),
-            "slot_sets_rotated": len(sets), "steps": steps, "warmup": warmup}
+    stride = c.H * 128 * 128
+    acc = None if w.accepted is None else w.accepted.data_ptr()
+    res = {}
+    names = {0: "free", kprobe.BARRIER: "barrier", kprobe.CORE_OCCUPANCY: "core_occupancy",
+             kprobe.BARRIER | kprobe.CORE_OCCUPANCY: "barrier_core_occupancy"}
+    for opt, name in names.items():
+        fns = [lambda s=s, o=opt: plib.kda_probe_state_stream(
+            w.state.data_ptr(), stride, c.num_slots, s.data_ptr(),
+            s.stride(0) if s.dim() == 2 else 1, acc, c.R, c.L, c.H, o, sp) for s in w.sets]
+        res[name] = round(time_back_to_back(torch, fns, steps, 10, stream), 5)
+    state_bytes = (c.R + c.S) * c.H * 128 * 128 * 4
+    if c.L == 1:
+        # in-place decode moves R H tiles in and out: a plain device copy of as many bytes
+        n = c.R * c.H * 128 * 128
+        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(0.5)
+        b = torch.empty_like(a)
+        res["device_copy"] = round(time_back_to_back(torch, [lambda: (b.copy_(a), 0)[1]],
+                                                     steps, 10, stream), 5)
+        del a, b
+    best = min(res, key=res.get)
+    return {"variants_ms": res, "best": best, "kernel_ms": res[best], "state_bytes": state_bytes,
+            "gbps": round(state_bytes / (res[best] * 1e-3) / 1e9, 1)}
 
 
-def probe(torch, kda):
+def flush_fn(torch):
+    """1 GiB of plain writes through the probe library: evicts the Infinity Cache."""
+    from kimi_delta_attention_conv_amd import probe as kprobe
+    plib = kprobe.load_probe_library()
+    buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    sp = torch.cuda.current_stream().cuda_stream
+
+    def fn():
+        if plib.kda_probe_write_runs(buf.data_ptr(), 1 << 30, 0.25, sp) != 0:
+            raise RuntimeError("flush failed")
+    fn.buf = buf
+    return fn
+
+
+def workload_row(torch, kda, index, steps, warmup, rounding, flush):
+    """Everything the line reports for one workload."""
+    w = Workload(torch, kda, index, rounding)
+    stream = torch.cuda.current_stream()
+    fns = w.launches(stream.cuda_stream)
+    c = w.case
+    print(f"[bench] {c.name}: {steps} rotated launches", file=sys.stderr, flush=True)
+    ms = time_back_to_back(torch, fns, steps, warmup, stream)
+    w.check_errors()
+    gbps = w.metric_bytes / (ms * 1e-3) / 1e9
+    row = {"workload": c.name, "requests": c.R, "tokens": c.L, "rows": c.S, "heads": c.H,
+           "kernel_ms": round(ms, 5), "tokens_per_s": round(c.S / (ms * 1e-3), 1),
+           "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+           "metric_bytes_per_step": w.metric_bytes, "slot_sets_rotated": len(w.sets),
+           "pool_bytes": w.pool_bytes, "steps": steps, "warmup": warmup}
+    row["launch_us"] = time_each(torch, fns, 50, stream)
+    if w.pool_bytes <= MALL_BYTES:
+        row["cache_resident"] = True
+        fl = time_each(torch, fns, 30, stream, before=flush)
+        row["flushed_launch_us"] = fl
+        row["flushed_gbps"] = round(w.metric_bytes / (fl["p50"] * 1e-6) / 1e9, 1)
+        row["flushed_frac"] = round(row["flushed_gbps"] / HBM_PEAK_GBPS, 4)
+    w.check_errors()
+    pat = pattern_ceiling(torch, w, min(steps, 100), stream)
+    row["pattern"] = pat
+    row["frac_of_pattern"] = round(pat["kernel_ms"] / ms, 4)
+    w.close()
+    del w
+    torch.cuda.empty_cache()
+    return row
+
+
+def probe(torch):
     """Achievable HBM GB/s of plain read, write and copy streams (1 GiB buffers)."""
-    lib = kda.load_library()
+    from kimi_delta_attention_conv_amd import probe as kprobe
+    lib = kprobe.load_probe_library()
     nbytes = 1 << 30
     a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
@@ -214,18 +301,9 @@ def probe(torch, kda):
     moved = {"read": nbytes, "write": nbytes, "copy": 2 * nbytes, "write_runs": nbytes,
              "copy_runs": 2 * nbytes}
     res = {}
+    stream = torch.cuda.current_stream()
     for name, fn in calls.items():
-        for _ in range(3):
-            assert fn() == 0
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        n = 10
-        e0.record()
-        for _ in range(n):
-            fn()
-        e1.record()
-        e1.synchronize()
-        ms = e0.elapsed_time(e1) / n
+        ms = time_back_to_back(torch, [fn], 10, 3, stream)
         res[name] = dict(gbps=round(moved[name] / (ms * 1e-3) / 1e9, 1), ms=round(ms, 4),
                          bytes=moved[name])
     del a, b, sink
@@ -257,16 +335,8 @@ def bench_projections(args, torch, kda):
         def launch(i):
             return lib.kda_linear(xs.data_ptr(), xs.stride(0), ws[i % copies].data_ptr(),
                                   y.data_ptr(), N, S, N, K, work.data_ptr(), ws_bytes, sp)
-        for i in range(args.warmup):
-            assert launch(i) == 0
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(args.steps):
-            launch(i)
-        e1.record()
-        e1.synchronize()
-        ms = e0.elapsed_time(e1) / args.steps
+        fns = [lambda i=i: launch(i) for i in range(copies)]
+        ms = time_back_to_back(torch, fns, args.steps, args.warmup, torch.cuda.current_stream())
         flops = 2.0 * S * N * K
         nbytes = (N * K + S * K + S * N) * 2
         tflops = flops / (ms * 1e-3) / 1e12
@@ -289,11 +359,12 @@ def bench_layer(args, torch, kda):
     """One layer's attention-core step as a serving loop runs it: in_proj
     (hidden 7168 -> packed row), the core (decode or verify), o_proj (D -> 7168).
     Weight copies and slot sets rotate so that every step streams from HBM."""
-    from kda_inputs import HIDDEN, make_config, make_linear
-    case = make_config(args.config)
+    from kda_inputs import HIDDEN, make_linear
+    w = Workload(torch, kda, args.config)
+    case = w.case
     S, H, D, pitch = case.S, case.H, case.D, case.pitch
     n_in = 4 * D + 128 + H
-    lib = kda.load_library()
+    lib = w.lib
     dev = "cuda"
     x, w_in = make_linear(S, n_in, HIDDEN, seed=21)
     _, w_o = make_linear(1, HIDDEN, D, seed=22)
@@ -301,36 +372,20 @@ def bench_layer(args, torch, kda):
     xs = x.to(dev)
     w_ins = [w_in.to(dev) for _ in range(copies)]
     w_os = [w_o.to(dev) for _ in range(copies)]
-    conv_storage = case.conv_storage.to(dev)
-    conv = conv_storage if case.conv_dim_first else conv_storage.transpose(-1, -2)
-    state = case.state.to(dev)
-    core = kda.KdaCore(conv_weight=case.conv_weight.to(dev),
-                       conv_bias=None if case.conv_bias is None else case.conv_bias.to(dev),
-                       f_b=case.f_b.to(dev), A_log=case.A_log.to(dev), dt_bias=case.dt_bias.to(dev),
-                       norm_weight=case.norm_weight.to(dev), gate_lower_bound=case.gate_lower_bound,
-                       norm_eps=case.norm_eps, l2_eps=case.l2_eps, conv=conv, state=state)
-    projected = torch.zeros(S, pitch, dtype=torch.bfloat16, device=dev)
-    core_out = torch.empty(S, D, dtype=torch.bfloat16, device=dev)
+    projected = w.projected
+    core_out = w.out
     out = torch.empty(S, HIDDEN, dtype=torch.bfloat16, device=dev)
-    slot_base, views = rotation_sets(case, torch)
-    slot_base = slot_base.to(dev)
-    sets = [torch.as_strided(slot_base, sh, st, off) for sh, st, off in views]
-    accepted = None if case.accepted is None else case.accepted.to(dev)
-    h = core.handle
     # one workspace serves both projections (they run in stream order)
     ws_bytes = max(int(lib.kda_linear_workspace_bytes(S, n_in, HIDDEN)),
                    int(lib.kda_linear_workspace_bytes(S, HIDDEN, D)))
     work = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     def parts(i, sp):
-        w1, w2, sl = w_ins[i % copies], w_os[i % copies], sets[i % len(sets)]
+        w1, w2 = w_ins[i % copies], w_os[i % copies]
         return [
             lambda: lib.kda_in_proj(xs.data_ptr(), HIDDEN, w1.data_ptr(), projected.data_ptr(),
                                     pitch, S, HIDDEN, H, work.data_ptr(), ws_bytes, sp),
-            (lambda: lib.kda_decode(h, projected.data_ptr(), pitch, case.R, sl.data_ptr(),
-                                    core_out.data_ptr(), sp)) if accepted is None else
-            (lambda: lib.kda_verify(h, projected.data_ptr(), pitch, case.R, case.L, sl.data_ptr(),
-                                    sl.stride(0), accepted.data_ptr(), core_out.data_ptr(), sp)),
+            w.make_launch(w.sets[i % len(w.sets)], sp),
             lambda: lib.kda_o_proj(core_out.data_ptr(), D, w2.data_ptr(), out.data_ptr(), HIDDEN,
                                    S, H, HIDDEN, work.data_ptr(), ws_bytes, sp),
         ]
@@ -342,7 +397,7 @@ def bench_layer(args, torch, kda):
         for f in parts(i, sp):
             assert f() == 0
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = events(torch)
     e0.record(stream)
     for i in range(steps):
         for f in parts(i, sp):
@@ -354,7 +409,7 @@ def bench_layer(args, torch, kda):
     names = ("in_proj", "core", "o_proj")
     alone = {}
     for k, name in enumerate(names):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = events(torch)
         a.record(stream)
         for i in range(steps):
             parts(i, sp)[k]()
@@ -374,17 +429,15 @@ def bench_layer(args, torch, kda):
         graph.replay()
     torch.cuda.synchronize()
     reps = max(1, steps // copies)
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0, g1 = events(torch)
     g0.record(stream)
     for _ in range(reps):
         graph.replay()
     g1.record(stream)
     torch.cuda.synchronize()
     graph_us = g0.elapsed_time(g1) / (reps * copies) * 1e3
-    errors = core.device_errors()
-    core.close()
-    if errors:
-        raise RuntimeError(f"{errors} requests were skipped")
+    w.check_errors()
+    w.close()
     return {"workload": case.name, "rows": S, "heads": H, "hidden": HIDDEN,
             "eager_us_per_step": round(eager_us, 2), "graph_us_per_step": round(graph_us, 2),
             "tokens_per_s_graph": round(S / (graph_us * 1e-6), 1),
@@ -492,7 +545,7 @@ def main():
         sys.exit(1)
 
     if args.probe_only:
-        print(json.dumps({"hbm_probe": probe(torch, kda)}), flush=True)
+        print(json.dumps({"hbm_probe": probe(torch)}), flush=True)
         return
     if args.layer:
         print(json.dumps({"layer": bench_layer(args, torch, kda)}), flush=True)
@@ -502,37 +555,10 @@ def main():
                           "workload_rows_of": make_config(args.config).name}), flush=True)
         return
 
-    case = make_config(args.config)
-    dev = "cuda"
-    conv_storage = case.conv_storage.to(dev)
-    conv = conv_storage if case.conv_dim_first else conv_storage.transpose(-1, -2)
-    state = case.state.to(dev)
-    core = kda.KdaCore(conv_weight=case.conv_weight.to(dev),
-                       conv_bias=None if case.conv_bias is None else case.conv_bias.to(dev),
-                       f_b=case.f_b.to(dev), A_log=case.A_log.to(dev),
-                       dt_bias=case.dt_bias.to(dev), norm_weight=case.norm_weight.to(dev),
-                       gate_lower_bound=case.gate_lower_bound, norm_eps=case.norm_eps,
-                       l2_eps=case.l2_eps, conv=conv, state=state, rounding=args.rounding)
-    projected = case.projected.to(dev)
-    out = torch.empty(case.S, case.D, dtype=torch.bfloat16, device=dev)
-    slot_base, views = rotation_sets(case, torch)
-    slot_base = slot_base.to(dev)
-    sets = [torch.as_strided(slot_base, shape, stride, off) for shape, stride, off in views]
-    accepted = None if case.accepted is None else case.accepted.to(dev)
-    h = core.handle
-    pitch = case.pitch
-    lib = kda.load_library()
-
-    def make_launch(s, sp):
-        if accepted is None:
-            return lambda: lib.kda_decode(h, projected.data_ptr(), pitch, case.R, s.data_ptr(),
-                                          out.data_ptr(), sp)
-        return lambda: lib.kda_verify(h, projected.data_ptr(), pitch, case.R, case.L,
-                                      s.data_ptr(), s.stride(0), accepted.data_ptr(),
-                                      out.data_ptr(), sp)
-
+    w = Workload(torch, kda, args.config, args.rounding)
+    case = w.case
     stream = torch.cuda.current_stream()
-    launches = [make_launch(s, stream.cuda_stream) for s in sets]
+    launches = w.launches(stream.cuda_stream)
     if args.graph:
         chain = args.graph
         graph = torch.cuda.CUDAGraph()
@@ -540,7 +566,7 @@ def main():
         with torch.cuda.graph(graph):
             sp_cap = torch.cuda.current_stream().cuda_stream
             for i in range(chain):
-                rc = make_launch(sets[i % len(sets)], sp_cap)()
+                rc = w.make_launch(w.sets[i % len(w.sets)], sp_cap)()
                 if rc != 0:
                     raise RuntimeError(f"capture failed: {kda.kda_status_string(rc)}")
         args.warmup = -(-args.warmup // chain)
@@ -556,7 +582,7 @@ def main():
     print(f"[bench] {case.name}: warmup {args.warmup} done, timing {args.steps} steps",
           file=sys.stderr, flush=True)
 
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = events(torch)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
@@ -567,49 +593,13 @@ def main():
     if failed:
         raise RuntimeError(f"{failed} timed launches failed")
     gpu_ms = e0.elapsed_time(e1)
-    errors = core.device_errors()
-    if errors:
-        raise RuntimeError(f"{errors} requests were skipped for invalid slots")
-
-    # per-launch distribution (after the timed region): each launch between
-    # its own pair of events on the launch stream
-    launch_us = None
-    hot = None
-    if not args.graph:
-        pairs = []
-        for i in range(50):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            launches[i % len(launches)]()
-            b.record(stream)
-            pairs.append((a, b))
-        torch.cuda.synchronize()
-        us = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
-        launch_us = {"p10": round(us[4], 2), "p50": round(us[24], 2), "p90": round(us[44], 2),
-                     "launches": len(us)}
-        # hot: the same slot set every step, so part of the pool can stay in the MALL
-        for _ in range(5):
-            launches[0]()
-        torch.cuda.synchronize()
-        h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        h0.record(stream)
-        for _ in range(50):
-            launches[0]()
-        h1.record(stream)
-        torch.cuda.synchronize()
-        hot_ms = h0.elapsed_time(h1) / 50
-        hot = {"kernel_ms": round(hot_ms, 5),
-               "gbps": round((case.R + case.S) * case.H * UNIT_BYTES / (hot_ms * 1e-3) / 1e9, 1),
-               "note": "one slot set every step (reported beside the rotated figure, not as it)"}
-        if core.device_errors():
-            raise RuntimeError("requests were skipped for invalid slots")
+    w.check_errors()
 
     per_replay = args.graph if args.graph else 1
     steps_run = args.steps * per_replay
     ms_per_step = wall * 1e3 / steps_run
     kernel_ms = gpu_ms / steps_run           # one launch of the core kernel per step
-    metric_bytes = (case.R + case.S) * case.H * UNIT_BYTES
-    achieved = metric_bytes / (kernel_ms * 1e-3) / 1e9
+    achieved = w.metric_bytes / (kernel_ms * 1e-3) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE)).get(case.name)
@@ -631,40 +621,47 @@ def main():
         "config": {"workload": case.name, "requests": case.R, "tokens": case.L,
                    "rows": case.S, "heads": case.H, "head_dim": 128, "pool_slots": case.num_slots,
                    "conv_layout": "dim_first" if case.conv_dim_first else "transposed",
-                   "slot_sets_rotated": len(sets), "io": "bf16", "state": "f32",
+                   "slot_sets_rotated": len(w.sets), "io": "bf16", "state": "f32",
                    "rounding": args.rounding,
                    "launch": f"hip_graph x{args.graph}" if args.graph else "eager"},
-        "gbps": round(metric_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "metric_bytes_per_step": metric_bytes,
+        "gbps": round(w.metric_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "metric_bytes_per_step": w.metric_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": KERNEL_NAME,
                      "kernel_ms": round(kernel_ms, 5)},
     }
-    if launch_us is not None:
-        result["launch_us"] = launch_us
-        result["hot"] = hot
+    if args.trace_only:
+        w.close()
+        print(json.dumps(result), flush=True)
+        return
     if not args.graph:
-        # the kernel against its own access pattern with no arithmetic (time ratio)
-        pattern = time_pattern(torch, lib, state, case, sets, accepted, min(args.steps, 100), 10)
-        result["roofline"]["pattern_probe"] = pattern
-        result["roofline"]["frac_of_pattern"] = round(pattern["kernel_ms"] / kernel_ms, 4)
+        result["launch_us"] = time_each(torch, launches, 50, stream)
+        pat = pattern_ceiling(torch, w, min(args.steps, 100), stream)
+        result["roofline"]["pattern"] = pat
+        result["roofline"]["frac_of_pattern"] = round(pat["kernel_ms"] / kernel_ms, 4)
+    w.check_errors()
+    w.close()
+    del w
+    torch.cuda.empty_cache()
     if not args.no_probe:
         print("[bench] HBM probes", file=sys.stderr, flush=True)
-        pr = probe(torch, kda)
+        pr = probe(torch)
         result["hbm_probe"] = pr
         best = {"read": pr["read"]["gbps"],
                 "write": max(pr["write"]["gbps"], pr["write_runs"]["gbps"]),
                 "copy": max(pr["copy"]["gbps"], pr["copy_runs"]["gbps"])}
         result["roofline"]["frac_of_probe"] = {k: round(achieved / v, 4) for k, v in best.items()}
-    core.close()
-    del state, conv_storage
-    torch.cuda.empty_cache()
-    if args.config == 3 and not args.graph and not args.skip_decode:
-        # the other workload the HBM target is stated for, kernel time only
-        print("[bench] decode R=256", file=sys.stderr, flush=True)
-        result["decode_r256"] = time_workload(torch, kda, 4, 100, 10)
         torch.cuda.empty_cache()
+    if not args.no_configs and not args.graph:
+        flush = flush_fn(torch)
+        table = {}
+        for index in range(5):
+            row = workload_row(torch, kda, index, 100, 10, args.rounding, flush)
+            table[row["workload"]] = row
+        del flush
+        torch.cuda.empty_cache()
+        result["configs"] = table
     if args.cpu_seconds > 0:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)

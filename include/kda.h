@@ -16,11 +16,9 @@
  *
  * Sources (page titles; sections named, no line numbers):
  *   [kda]      "vllm.models.kimi_k3.amd.specialized_decode.mono.attention.kda":
- *              module docstring (K1 kda_pre, "kda tasks" row: conv update,
- *              f_b MFMA + lower-bound gate, l2norm, the recurrence on 16 state
- *              rows with a state written per token, gated RMSNorm -> core_out)
- *              and the host launcher entry kda_pre (conv_state
- *              [slots, dim, state_len] or a transposed view).
+ *              module docstring (kernel K1 kda_pre; the role table's "kda
+ *              tasks" row names the steps above and their order) and the host
+ *              launcher entry kda_pre (the two conv cache layouts).
  *   [prepared] "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.kda.prepared":
  *              PreparedKda.__init__ (weights, fp32 norm weight, the scalars
  *              gate_lower_bound, 128^-0.5, o_norm.eps), _operands (the packed
@@ -40,8 +38,12 @@
  *     except for KDA_ERR_HIP (a HIP call failed; see kda_last_hip_error).
  *   - Nothing unwinds across the ABI; no function allocates on the host per
  *     call. Only kda_prepare allocates device memory; kda_destroy frees it.
- *   - Within one call the destination slots of all requests must be distinct
- *     (a precondition, not checked): overlapping destinations race.
+ *   - Within one call every (request, token) must name its own destination
+ *     slot ([prepared] run: a block-table slice). A slot named twice races and
+ *     has no defined result, unless the caches were registered with
+ *     check_distinct, which turns such requests into skipped, counted ones.
+ *   - No call records a memset: counters and claims are cleared by kernels, so
+ *     kda_decode, kda_verify and the projections can be captured in a HIP graph.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -71,9 +73,9 @@ typedef enum {
 
 typedef struct kda_handle_s* kda_handle;
 
-/* Where intermediate values are rounded ([kda] module docstring: elementwise
- * rounding follows the original, unfused path at every bf16 hand-off between
- * its kernels).
+/* Where intermediate values are rounded ([kda] module docstring, its sentence
+ * on rounding: the fused kernels are to round as the unfused kernels did
+ * wherever those passed bf16 tensors to one another).
  *   KDA_ROUND_FUSED         every intermediate stays fp32 inside the kernel;
  *   KDA_ROUND_BF16_HANDOFF  the values an unfused pipeline hands over in bf16
  *                           are rounded to bf16 (RNE) where produced: the conv
@@ -112,8 +114,9 @@ typedef struct {
                                  0) or [H][128] (stride 128); element type norm_weight_dtype */
     int32_t norm_head_stride; /* 0 or 128 */
     float gate_lower_bound;   /* lb (e.g. -5); finite */
-    float norm_eps;           /* o_norm.eps (e.g. 1e-6); >= 0 */
-    float l2_eps;             /* epsilon inside the l2norm square root (1e-6); >= 0 */
+    float norm_eps;           /* o_norm.eps (e.g. 1e-6); finite and > 0 */
+    float l2_eps;             /* epsilon inside the l2norm square root (1e-6); finite and > 0
+                                 (with 0, an all-zero q or k row would give 0 / 0) */
     int32_t rounding;         /* a kda_rounding value; zero-initialised = KDA_ROUND_FUSED */
     int32_t A_log_dtype;      /* kda_dtype of A_log; zero-initialised = KDA_F32 */
     int32_t dt_bias_dtype;    /* kda_dtype of dt_bias */
@@ -134,7 +137,16 @@ typedef struct {
  *           strides are accepted; those two are the fast paths.
  *   state : fp32 [slots][H][128 v][128 k] per slot, slot stride
  *           state_slot_stride >= H * 128 * 128; row v of a head is
- *           contiguous over k. Base 16-byte aligned, stride a multiple of 4. */
+ *           contiguous over k. Base 16-byte aligned, stride a multiple of 4.
+ *
+ *   check_distinct : 0 (default) or 1. With 1, every kda_decode / kda_verify
+ *           call first counts, per slot, how many (valid request, token)
+ *           pairs name it as a destination, and every request naming a slot
+ *           counted more than once (twice in its own row included) is skipped
+ *           entirely and counted in kda_device_errors, like a request with an
+ *           invalid index; the counts are reset at the end of the call. Costs
+ *           num_slots * 4 bytes of handle memory and two small kernels a call.
+ *           With 0 the distinct destinations are a precondition, not checked. */
 typedef struct {
     void* conv;
     int64_t conv_slot_stride;
@@ -143,6 +155,7 @@ typedef struct {
     float* state;
     int64_t state_slot_stride;
     int32_t num_slots;        /* >= 1; valid slot indices are 0 .. num_slots - 1 */
+    int32_t check_distinct;   /* 0 or 1 (above); zero-initialised = no check */
 } kda_caches;
 
 /* Creates a handle: validates, allocates the handle's device memory, re-lays
@@ -150,8 +163,9 @@ typedef struct {
  * the caches. *out is set only on KDA_OK.
  * Errors: KDA_ERR_NULL (w, c, out, a weight or cache pointer), KDA_ERR_SHAPE
  * (heads < 1, num_slots < 1, a stride too small or negative, norm_head_stride
- * not 0 or 128, a non-finite scalar or negative epsilon, rounding not a
- * kda_rounding value, a dtype not a kda_dtype value), KDA_ERR_ALIGN (a weight
+ * not 0 or 128, a non-finite scalar or an epsilon <= 0, rounding not a
+ * kda_rounding value, a dtype not a kda_dtype value, check_distinct not 0 or
+ * 1), KDA_ERR_ALIGN (a weight
  * pointer not aligned to its element size, the state base or stride),
  * KDA_ERR_UNSUPPORTED (conv_width != 4),
  * KDA_ERR_NOMEM, KDA_ERR_HIP. */
@@ -163,13 +177,14 @@ kda_status kda_prepare(const kda_weights* w, const kda_caches* c, void* hip_stre
  * conv window in place at slot slots[b].
  *   projected : device bf16 [batch][pitch], row b = q|k|v (3D) | gate (D) |
  *               f_a (128) | beta_raw (H) | padding ([prepared] _operands).
- *               pitch >= 4D + 128 + H and even; base 4-byte aligned.
+ *               pitch >= 4D + 128 + H (any parity); base 2-byte aligned.
  *   slots     : device int32 [batch].
  *   core_out  : device bf16 [batch][D]; base 4-byte aligned.
  * A request whose slot is outside 0 .. num_slots - 1 is skipped entirely (no
  * read, no write, its core_out row untouched) and counted in the device error
- * counter (kda_device_errors). batch == 0 is a no-op.
- * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE (batch < 0, pitch too small or odd),
+ * counter (kda_device_errors); so is, with check_distinct, a request whose
+ * slot another request of the call also names. batch == 0 is a no-op.
+ * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE (batch < 0, pitch too small),
  * KDA_ERR_ALIGN, KDA_ERR_DEVICE (called with another device current than the
  * one kda_prepare ran on), KDA_ERR_HIP. */
 kda_status kda_decode(kda_handle h, const void* projected, int64_t pitch, int32_t batch,
@@ -232,6 +247,7 @@ kda_status kda_linear(const void* x, int64_t x_pitch, const void* w, void* y, in
 /* Bytes of workspace with which kda_linear splits K for this shape; 0 when
  * the shape is never split (or the shape is invalid). Host-only. */
 size_t kda_linear_workspace_bytes(int32_t M, int32_t N, int32_t K);
+
 
 /* in_proj: N = 4D + 128 + H packed outputs (D = 128 heads), K = hidden;
  * projected rows are `pitch` elements apart (pitch >= N). Workspace as for

@@ -1,5 +1,6 @@
 /*
- * kda_probe.h -- HBM stream probes exported by libkda.so (measurement only).
+ * kda_probe.h -- HBM stream probes exported by libkda_probe.so (measurement
+ * only; a library of its own, apart from the product library libkda.so).
  *
  * Plain read, write and copy kernels over a device buffer. The grid-stride
  * ones use the same 16-byte non-temporal accesses the core kernel uses for its
@@ -58,12 +59,24 @@ int32_t kda_probe_sink_floats(void);
  * multiple of 4 and >= heads * 16384. slots, accepted: int32, 4-byte aligned.
  * 1 <= tokens <= 8, slots_row_stride >= tokens, 1 <= heads <= 4096,
  * requests >= 0 (0 enqueues nothing), requests * heads <= INT32_MAX.
- * Returns KDA_OK, KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_ALIGN or KDA_ERR_HIP;
- * nothing is enqueued on error. Overwrites the destination tiles. */
+ *
+ * options (bit set):
+ *   KDA_PROBE_BARRIER         a workgroup barrier between the tile's loads and
+ *                             the first store (every wave's loads returned
+ *                             first, as at the core kernel's first barrier);
+ *   KDA_PROBE_CORE_OCCUPANCY  residency held to the core kernel's (one 16-wave
+ *                             or two 8-wave workgroups a compute unit) by a
+ *                             static LDS allocation.
+ * The fastest of the four variants is the ceiling of the access pattern.
+ * Returns KDA_OK, KDA_ERR_NULL, KDA_ERR_SHAPE (also unknown option bits),
+ * KDA_ERR_ALIGN or KDA_ERR_HIP; nothing is enqueued on error. Overwrites the
+ * destination tiles. */
+#define KDA_PROBE_BARRIER 1
+#define KDA_PROBE_CORE_OCCUPANCY 2
 int kda_probe_state_stream(float* state, int64_t state_slot_stride, int32_t num_slots,
                            const int32_t* slots, int64_t slots_row_stride,
                            const int32_t* accepted, int32_t requests, int32_t tokens,
-                           int32_t heads, void* hip_stream);
+                           int32_t heads, int32_t options, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -109,10 +109,8 @@ CONFIGS = {
 
 
 def default_pitch(H: int) -> int:
-    """4D + 128 + H elements, rounded up to even (the ABI takes 4-byte rows)."""
-    D = H * HEAD_DIM
-    p = 4 * D + FA_RANK + H
-    return p + (p & 1)
+    """4D + 128 + H elements: the packed row with no padding (odd for odd H)."""
+    return 4 * H * HEAD_DIM + FA_RANK + H
 
 
 def make_case(R: int, L: int, H: int, num_slots: int, seed: int, *, name: str = "custom",

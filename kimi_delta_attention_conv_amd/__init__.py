@@ -61,7 +61,7 @@ class KdaCaches(ctypes.Structure):
         ("conv", ctypes.c_void_p), ("conv_slot_stride", ctypes.c_int64),
         ("conv_dim_stride", ctypes.c_int64), ("conv_pos_stride", ctypes.c_int64),
         ("state", ctypes.c_void_p), ("state_slot_stride", ctypes.c_int64),
-        ("num_slots", ctypes.c_int32),
+        ("num_slots", ctypes.c_int32), ("check_distinct", ctypes.c_int32),
     ]
 
 
@@ -100,18 +100,6 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         f.restype = ctypes.c_int
     lib.kda_linear_workspace_bytes.argtypes = [i32, i32, i32]
     lib.kda_linear_workspace_bytes.restype = sz
-    # HBM stream probes (include/kda_probe.h), measurement only
-    lib.kda_probe_copy.argtypes = [vp, vp, i64, vp]
-    lib.kda_probe_write.argtypes = [vp, i64, ctypes.c_float, vp]
-    lib.kda_probe_read.argtypes = [vp, i64, vp, vp]
-    lib.kda_probe_copy_runs.argtypes = [vp, vp, i64, vp]
-    lib.kda_probe_write_runs.argtypes = [vp, i64, ctypes.c_float, vp]
-    lib.kda_probe_state_stream.argtypes = [vp, i64, i32, vp, i64, vp, i32, i32, i32, vp]
-    for f in (lib.kda_probe_copy, lib.kda_probe_write, lib.kda_probe_read, lib.kda_probe_copy_runs,
-              lib.kda_probe_write_runs, lib.kda_probe_state_stream):
-        f.restype = ctypes.c_int
-    lib.kda_probe_sink_floats.argtypes = []
-    lib.kda_probe_sink_floats.restype = i32
     _lib = lib
     return lib
 
@@ -235,11 +223,13 @@ class KdaCore:
              [D, 128]; A_log [H], dt_bias [D], norm_weight [128] or [H, 128], each
              fp32 or bf16 (converted to fp32 at prepare time).
     rounding: "fused" (default) or "bf16_handoff" (kda_rounding in kda.h).
+    check_distinct: make every call skip and count requests whose destination
+             slots collide (kda_caches.check_distinct in kda.h).
     """
 
     def __init__(self, *, conv_weight, conv_bias, f_b, A_log, dt_bias, norm_weight,
                  gate_lower_bound, norm_eps, conv, state, l2_eps=1e-6, stream=None,
-                 rounding="fused"):
+                 rounding="fused", check_distinct=False):
         import torch
 
         self._torch = torch
@@ -288,7 +278,8 @@ class KdaCore:
         cs = conv.stride()
         c = KdaCaches(conv=conv.data_ptr(), conv_slot_stride=cs[0], conv_dim_stride=cs[1],
                       conv_pos_stride=cs[2], state=state.data_ptr(),
-                      state_slot_stride=state.stride(0), num_slots=int(state.shape[0]))
+                      state_slot_stride=state.stride(0), num_slots=int(state.shape[0]),
+                      check_distinct=int(bool(check_distinct)))
         if conv.shape[0] != state.shape[0]:
             raise ValueError("conv and state pools must have the same slot count")
         # the handle belongs to the device current at prepare time: the pools' device

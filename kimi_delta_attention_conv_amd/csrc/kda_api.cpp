@@ -17,6 +17,13 @@
 #include "kda.h"
 #include "kda_internal.h"
 
+static thread_local char g_last_hip_error[256] = "";
+
+void kda::record_hip_error(hipError_t e, const char* what) {
+    std::snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s: %s (%d)", what,
+                  hipGetErrorString(e), (int)e);
+}
+
 struct kda_handle_s {
     int device = 0;
     int32_t cu_count = 0;        // compute units of `device` (the core's choice of waves a unit)
@@ -24,6 +31,7 @@ struct kda_handle_s {
     void* dev_mem = nullptr;
     kda::PreparedWeights w{};
     int32_t* err_count = nullptr;
+    int32_t* claims = nullptr;   // [num_slots] destination counts (check_distinct), else null
     kda_caches caches{};
     float lb = 0.0f, norm_eps = 0.0f, l2_eps = 0.0f;
     int32_t rounding = KDA_ROUND_FUSED;
@@ -31,11 +39,8 @@ struct kda_handle_s {
 
 namespace {
 
-thread_local char g_last_hip_error[256] = "";
-
 kda_status hip_fail(hipError_t e, const char* what) {
-    std::snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s: %s (%d)", what,
-                  hipGetErrorString(e), (int)e);
+    kda::record_hip_error(e, what);
     return KDA_ERR_HIP;
 }
 
@@ -61,8 +66,7 @@ kda_status check_call(const kda_handle_s* h, const void* projected, int64_t pitc
     if (projected == nullptr || slots == nullptr || core_out == nullptr) return KDA_ERR_NULL;
     const int64_t D = (int64_t)h->heads * kda::kHeadDim;
     if (pitch < 4 * D + kda::kFaRank + h->heads) return KDA_ERR_SHAPE;
-    if (pitch % 2 != 0) return KDA_ERR_SHAPE;
-    if (!aligned(projected, 4) || !aligned(core_out, 4) || !aligned(slots, 4)) return KDA_ERR_ALIGN;
+    if (!aligned(projected, 2) || !aligned(core_out, 4) || !aligned(slots, 4)) return KDA_ERR_ALIGN;
     // the grid is requests x heads workgroups
     if ((int64_t)requests * h->heads > INT32_MAX) return KDA_ERR_SHAPE;
     return KDA_OK;
@@ -99,13 +103,31 @@ kda::CoreParams core_params(const kda_handle_s* h, const void* projected, int64_
     p.norm_eps = h->norm_eps;
     p.l2_eps = h->l2_eps;
     p.handoff_bf16 = h->rounding == KDA_ROUND_BF16_HANDOFF;
+    // f_a is read as 4-byte words when every row starts 4-byte aligned
+    p.fa_u16 = (pitch % 2 != 0) || !aligned(projected, 4);
     p.cu_count = h->cu_count;
+    p.claims = h->claims;
     // the dim-first pool [slots][3D][3] with 16-byte aligned slots takes the
     // kernel's coalesced window stores (each head's q, k, v windows are three
     // contiguous 768-byte runs whose starts are multiples of 16 bytes)
     p.conv_dim_first16 = h->caches.conv_pos_stride == 1 && h->caches.conv_dim_stride == 3 &&
                          h->caches.conv_slot_stride % 8 == 0 && aligned(h->caches.conv, 16);
     return p;
+}
+
+// The core launch, with the distinct-destination check around it when the
+// handle has one: claims, the core kernel (which skips every request naming a
+// slot claimed more than once), then the claims' reset. All three are kernels
+// on the caller's stream, so the sequence can be captured in a graph.
+hipError_t run_core(const kda_handle_s* h, int tokens, const kda::CoreParams& p, hipStream_t s) {
+    if (h->claims == nullptr) return kda::launch_core(tokens, p, s);
+    hipError_t e = kda::launch_claims(tokens, p, h->claims, false, s);
+    if (e != hipSuccess) return e;
+    e = kda::launch_core(tokens, p, s);
+    // the reset is enqueued even when the core launch failed, so that the
+    // claims are zero again for the next call
+    const hipError_t c = kda::launch_claims(tokens, p, h->claims, true, s);
+    return e != hipSuccess ? e : c;
 }
 
 }  // namespace
@@ -138,8 +160,10 @@ kda_status kda_prepare(const kda_weights* w, const kda_caches* c, void* hip_stre
     if (w->heads < 1 || w->heads > 4096) return KDA_ERR_SHAPE;
     if (w->conv_width != kda::kWidth) return KDA_ERR_UNSUPPORTED;
     if (w->norm_head_stride != 0 && w->norm_head_stride != kda::kHeadDim) return KDA_ERR_SHAPE;
+    // both epsilons strictly positive: with zero, an all-zero q, k or o row
+    // would divide zero by zero
     if (!std::isfinite(w->gate_lower_bound) || !std::isfinite(w->norm_eps) ||
-        !std::isfinite(w->l2_eps) || w->norm_eps < 0.0f || w->l2_eps < 0.0f)
+        !std::isfinite(w->l2_eps) || !(w->norm_eps > 0.0f) || !(w->l2_eps > 0.0f))
         return KDA_ERR_SHAPE;
     if (w->rounding != KDA_ROUND_FUSED && w->rounding != KDA_ROUND_BF16_HANDOFF)
         return KDA_ERR_SHAPE;
@@ -147,6 +171,7 @@ kda_status kda_prepare(const kda_weights* w, const kda_caches* c, void* hip_stre
         if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_SHAPE;
     const int64_t H = w->heads, D = H * kda::kHeadDim, C = 3 * D;
     if (c->num_slots < 1) return KDA_ERR_SHAPE;
+    if (c->check_distinct != 0 && c->check_distinct != 1) return KDA_ERR_SHAPE;
     if (c->conv_slot_stride < 0 || c->conv_dim_stride < 0 || c->conv_pos_stride < 0)
         return KDA_ERR_SHAPE;
     // every (channel, position) of a slot must be addressable without overlap in
@@ -179,8 +204,8 @@ kda_status kda_prepare(const kda_weights* w, const kda_caches* c, void* hip_stre
     const int64_t b_conv_w = align_up(C * kda::kWidth * 4), b_conv_b = align_up(C * 4),
                   b_fb = align_up(D * kda::kFaRank * 2), b_a = align_up(H * 4),
                   b_dt = align_up(D * 4), b_nw = align_up(H * kda::kHeadDim * 4),
-                  b_err = kAlign;
-    const int64_t total = b_conv_w + b_conv_b + b_fb + b_a + b_dt + b_nw + b_err;
+                  b_err = kAlign, b_claims = c->check_distinct ? align_up((int64_t)c->num_slots * 4) : 0;
+    const int64_t total = b_conv_w + b_conv_b + b_fb + b_a + b_dt + b_nw + b_err + b_claims;
     e = hipMalloc(&h->dev_mem, (size_t)total);
     if (e != hipSuccess) {
         delete h;
@@ -200,6 +225,8 @@ kda_status kda_prepare(const kda_weights* w, const kda_caches* c, void* hip_stre
     h->w.norm_w = reinterpret_cast<float*>(base);
     base += b_nw;
     h->err_count = reinterpret_cast<int32_t*>(base);
+    base += b_err;
+    h->claims = c->check_distinct ? reinterpret_cast<int32_t*>(base) : nullptr;
     h->heads = w->heads;
     h->caches = *c;
     h->lb = w->gate_lower_bound;
@@ -220,7 +247,9 @@ kda_status kda_prepare(const kda_weights* w, const kda_caches* c, void* hip_stre
     in.A_log_bf16 = w->A_log_dtype == KDA_BF16;
     in.dt_bias_bf16 = w->dt_bias_dtype == KDA_BF16;
     in.norm_weight_bf16 = w->norm_weight_dtype == KDA_BF16;
-    e = hipMemsetAsync(h->err_count, 0, sizeof(int32_t), s);
+    // counters start at zero (kernels, not memsets: graph-safe everywhere)
+    e = kda::launch_zero(h->err_count, 1, s);
+    if (e == hipSuccess && h->claims != nullptr) e = kda::launch_zero(h->claims, c->num_slots, s);
     if (e == hipSuccess) e = kda::launch_prepare(in, h->w, s);
     if (e != hipSuccess) {
         kda_status st = hip_fail(e, "prepare launch");
@@ -238,7 +267,7 @@ kda_status kda_decode(kda_handle h, const void* projected, int64_t pitch, int32_
     if (st != KDA_OK || batch == 0) return st;
     if ((st = check_device(h)) != KDA_OK) return st;
     const kda::CoreParams p = core_params(h, projected, pitch, batch, slots, 1, nullptr, core_out);
-    hipError_t e = kda::launch_core(1, p, static_cast<hipStream_t>(hip_stream));
+    hipError_t e = run_core(h, 1, p, static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? KDA_OK : hip_fail(e, "kda_decode launch");
 }
 
@@ -257,7 +286,7 @@ kda_status kda_verify(kda_handle h, const void* projected, int64_t pitch, int32_
     if ((st = check_device(h)) != KDA_OK) return st;
     const kda::CoreParams p =
         core_params(h, projected, pitch, requests, slots, slots_row_stride, accepted, core_out);
-    hipError_t e = kda::launch_core(tokens, p, static_cast<hipStream_t>(hip_stream));
+    hipError_t e = run_core(h, tokens, p, static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? KDA_OK : hip_fail(e, "kda_verify launch");
 }
 
@@ -319,7 +348,7 @@ kda_status kda_device_errors(kda_handle h, int32_t* count_out, void* hip_stream)
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     int32_t host = 0;
     hipError_t e = hipMemcpyAsync(&host, h->err_count, sizeof host, hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipMemsetAsync(h->err_count, 0, sizeof(int32_t), s);
+    if (e == hipSuccess) e = kda::launch_zero(h->err_count, 1, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail(e, "kda_device_errors");
     *count_out = host;

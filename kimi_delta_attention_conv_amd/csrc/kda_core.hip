@@ -2,14 +2,20 @@
 //
 // Sources (page titles, sections):
 //   [kda]      "vllm.models.kimi_k3.amd.specialized_decode.mono.attention.kda",
-//              module docstring, "kda tasks" row: inputs that need no hand-off
-//              are loaded first (conv window, state rows, f_b rows), then the
-//              conv update, f_b MFMA + lower-bound gate, l2norm, the
-//              recurrence on 16 state rows with a state written per token, and
-//              the gated RMSNorm over the head's 128 outputs -> core_out.
+//              module docstring, the role table's "kda tasks" row (what a
+//              recurrence CTA does and in which order) and the functions
+//              kda_conv, kda_gates, kda_recur and kda_norm.
 //   [prepared] "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.kda.prepared",
 //              PreparedKda._operands (packed projection row), PreparedKda.__init__
 //              (weights prepared once: fp32 norm weight, exp of A_log).
+//
+// Per (request, head) unit this kernel resolves the slots, loads everything
+// it needs from memory before any arithmetic (the small per-token inputs
+// first, then the 64 KiB fp32 state tile), runs the width-4 conv with SiLU,
+// the gate contraction on the matrix cores and the decay gate, then for each
+// token the l2 scales, decay, delta-rule update and output, storing the
+// state after every token, and finally the gated RMSNorm of each token's 128
+// outputs into bf16 core_out and the shifted conv windows.
 //
 // One workgroup owns one (request, head) unit for all L tokens: 8 waves of 64,
 // wave w holding state rows v = 16w .. 16w + 15 in registers across the token
@@ -24,6 +30,8 @@
 // eight full 128-byte lines (eight rows x 128 B), and a row's dot product is
 // an 8-lane reduction done with three DPP steps.
 #include "kda_internal.h"
+
+#include <algorithm>
 
 namespace kda {
 namespace {
@@ -137,6 +145,10 @@ __global__ __launch_bounds__(64 * WAVES) void kda_core_kernel(const CoreParams p
         ok = ok && (unsigned)dst[t] < (unsigned)p.num_slots;
         if (t == a - 1) src = dst[t];
     }
+    if (ok && p.claims != nullptr) {   // distinct-destination check (opt-in)
+#pragma unroll
+        for (int t = 0; t < L; ++t) ok = ok && p.claims[dst[t]] == 1;
+    }
     if (!ok) {  // uniform across the workgroup: skip the whole request
         if (h == 0 && tid == 0) atomicAdd(p.err_count, 1);
         return;
@@ -194,12 +206,22 @@ __global__ __launch_bounds__(64 * WAVES) void kda_core_kernel(const CoreParams p
         for (int s = 0; s < 4; ++s) bfrag[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
     bf16x8 afrag[4];
-    if (mfma_wave && mn < L) {   // rows are only 4-byte aligned: dword loads
+    if (mfma_wave && mn < L && !p.fa_u16) {   // rows are only 4-byte aligned: dword loads
         const uint32_t* fa = reinterpret_cast<const uint32_t*>(prow + mn * p.pitch + 4 * (int64_t)D + 8 * kg);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             u32x4 v = {fa[16 * s + 0], fa[16 * s + 1], fa[16 * s + 2], fa[16 * s + 3]};
             afrag[s] = __builtin_bit_cast(bf16x8, v);
+        }
+    } else if (mfma_wave && mn < L) {         // odd pitch or base: 2-byte loads
+        const uint16_t* fa = prow + mn * p.pitch + 4 * (int64_t)D + 8 * kg;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w[e] = (uint32_t)fa[32 * s + 2 * e] | ((uint32_t)fa[32 * s + 2 * e + 1] << 16);
+            afrag[s] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
         }
     } else {
 #pragma unroll
@@ -431,6 +453,47 @@ __global__ void kda_prepare_kernel(const PrepareParams in, const PreparedWeights
     }
 }
 
+__global__ void kda_zero_kernel(int32_t* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+// One thread per request: the request's validity under the core kernel's
+// rules, then one claim per token on its destination slot (or the claims'
+// reset after the core kernel has read them). The claim counts reach the core
+// kernel through stream order; a slot claimed more than once in the call
+// makes every request naming it skip.
+template <int L>
+__global__ __launch_bounds__(256) void kda_claim_kernel(const CoreParams p, int32_t* claims, int clear) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= p.requests) return;
+    const int32_t* srow = p.slots + (int64_t)r * p.slots_row_stride;
+    const int a = p.accepted != nullptr ? p.accepted[r] : 1;
+    bool ok = a >= 1 && a <= L;
+    int dst[L];
+#pragma unroll
+    for (int t = 0; t < L; ++t) {
+        dst[t] = srow[t];
+        ok = ok && (unsigned)dst[t] < (unsigned)p.num_slots;
+    }
+    if (!ok) return;
+#pragma unroll
+    for (int t = 0; t < L; ++t) {
+        if (clear)
+            claims[dst[t]] = 0;
+        else
+            atomicAdd(claims + dst[t], 1);
+    }
+}
+
+template <int L>
+hipError_t launch_claims_t(const CoreParams& p, int32_t* claims, bool clear, hipStream_t s) {
+    const unsigned blocks = (unsigned)((p.requests + 255) / 256);
+    hipLaunchKernelGGL((kda_claim_kernel<L>), dim3(blocks), dim3(256), 0, s, p, claims, clear ? 1 : 0);
+    return hipGetLastError();
+}
+
 // Waves a unit (measured on MI355X, same box, alternating runs): sixteen 8-row
 // waves for every one-token call (in-place decode: 73.8 against 77.5 us for
 // 256 requests x 12 heads, 21.4 against 22.6 for 64, although only one such
@@ -459,6 +522,26 @@ hipError_t launch_core_t(const CoreParams& p, hipStream_t s) {
 hipError_t launch_prepare(const PrepareParams& in, const PreparedWeights& out, hipStream_t s) {
     hipLaunchKernelGGL(kda_prepare_kernel, dim3(256), dim3(256), 0, s, in, out);
     return hipGetLastError();
+}
+
+hipError_t launch_zero(int32_t* p, int64_t n, hipStream_t s) {
+    const int64_t blocks = std::min<int64_t>(1024, (n + 255) / 256);
+    hipLaunchKernelGGL(kda_zero_kernel, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_claims(int tokens, const CoreParams& p, int32_t* claims, bool clear, hipStream_t s) {
+    switch (tokens) {
+        case 1: return launch_claims_t<1>(p, claims, clear, s);
+        case 2: return launch_claims_t<2>(p, claims, clear, s);
+        case 3: return launch_claims_t<3>(p, claims, clear, s);
+        case 4: return launch_claims_t<4>(p, claims, clear, s);
+        case 5: return launch_claims_t<5>(p, claims, clear, s);
+        case 6: return launch_claims_t<6>(p, claims, clear, s);
+        case 7: return launch_claims_t<7>(p, claims, clear, s);
+        case 8: return launch_claims_t<8>(p, claims, clear, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_core(int tokens, const CoreParams& p, hipStream_t s) {

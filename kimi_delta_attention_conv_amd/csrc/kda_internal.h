@@ -50,7 +50,9 @@ struct CoreParams {
     float l2_eps;
     int32_t conv_dim_first16;   // conv pool is dim first [slots][3D][3], 16-byte aligned
     int32_t handoff_bf16;       // round conv out, g1 and o to bf16 where produced
+    int32_t fa_u16;             // f_a columns only 2-byte aligned (odd pitch or base)
     int32_t cu_count;           // compute units of the device (host side: waves a unit)
+    const int32_t* claims;      // per-slot destination counts of this call, or nullptr
 };
 
 // Raw inputs of the weight re-layout kernel (device pointers).
@@ -79,9 +81,18 @@ struct LinearParams {
 };
 
 hipError_t launch_prepare(const PrepareParams& in, const PreparedWeights& out, hipStream_t s);
+// n int32 zeros at p (a kernel, so that the clear can sit in a captured graph).
+hipError_t launch_zero(int32_t* p, int64_t n, hipStream_t s);
+// Destination claims of one call (p.claims non-null): add one per (valid
+// request, token) to claims[dst] (clear = false), or store zero there (clear =
+// true, after the core kernel). A request is valid under the core kernel's
+// rules (slots in range, accepted count in 1 .. L).
+hipError_t launch_claims(int tokens, const CoreParams& p, int32_t* claims, bool clear, hipStream_t s);
 hipError_t launch_linear(const LinearParams& p, hipStream_t s);
 // Workspace floats launch_linear uses for a K split of this shape (0: none).
 int64_t linear_workspace_floats(int32_t M, int32_t N, int32_t K);
 hipError_t launch_core(int tokens, const CoreParams& p, hipStream_t s);
+// Records a failed HIP call for kda_last_hip_error (this thread).
+void record_hip_error(hipError_t e, const char* what);
 
 }  // namespace kda

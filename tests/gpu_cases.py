@@ -29,7 +29,8 @@ class GpuCase:
     """Device copies of a case and a KdaCore bound to them."""
 
     def __init__(self, case: Case, *, projected=None, conv_storage=None, state=None,
-                 norm_weight=None, dt_bias=None, gate_lower_bound=None, rounding="fused"):
+                 norm_weight=None, dt_bias=None, gate_lower_bound=None, rounding="fused",
+                 check_distinct=False):
         self.case = case
         self.projected = (case.projected if projected is None else projected).cuda()
         st = case.conv_storage if conv_storage is None else conv_storage
@@ -44,7 +45,7 @@ class GpuCase:
             norm_weight=(case.norm_weight if norm_weight is None else torch.as_tensor(norm_weight)).cuda(),
             gate_lower_bound=case.gate_lower_bound if gate_lower_bound is None else gate_lower_bound,
             norm_eps=case.norm_eps, l2_eps=case.l2_eps, conv=self.conv, state=self.state,
-            rounding=rounding)
+            rounding=rounding, check_distinct=check_distinct)
         self.out = torch.full((case.S, case.D), OUT_SENTINEL, dtype=torch.int16).view(
             torch.bfloat16).cuda()
 

@@ -19,8 +19,10 @@ OUT_ATOL = 2e-2
 STATE_RTOL = 1e-3
 
 
-def request_slots(case, slots=None, accepted="case"):
-    """Per request: (valid, src, [dst per token]) under the oracle's rules."""
+def request_slots(case, slots=None, accepted="case", skip=()):
+    """Per request: (valid, src, [dst per token]) under the oracle's rules; the
+    requests in `skip` (e.g. colliding destinations under check_distinct) count
+    as invalid."""
     s = (case.slots if slots is None else slots).numpy()
     acc = case.accepted if isinstance(accepted, str) else accepted
     acc = None if acc is None else np.asarray(acc)
@@ -36,12 +38,13 @@ def request_slots(case, slots=None, accepted="case"):
             a = int(acc[r])
             ok = ok and 1 <= a <= case.L
             src = dst[a - 1] if ok else -1
-        res.append((ok, src, dst))
+        res.append((ok and r not in skip, src, dst))
     return res
 
 
-def assert_parity(case, ref, got, state_before, *, slots=None, accepted="case", label=""):
-    reqs = request_slots(case, slots, accepted)
+def assert_parity(case, ref, got, state_before, *, slots=None, accepted="case", label="",
+                  skip=()):
+    reqs = request_slots(case, slots, accepted, skip)
     n_bad = sum(1 for ok, _, _ in reqs if not ok)
     assert got["errors"] == n_bad == ref["skipped"], (label, got["errors"], n_bad, ref["skipped"])
 

@@ -12,11 +12,14 @@ int main(void) {
     bad |= kda_prepare(NULL, &c, NULL, &h) != KDA_ERR_NULL;
     w.heads = 2; w.conv_width = 4; w.conv_weight = (void*)0x10000; w.f_b = (void*)0x10000;
     w.A_log = (void*)0x10000; w.dt_bias = (void*)0x10000; w.norm_weight = (void*)0x10000;
+    w.norm_eps = 1e-6f; w.l2_eps = 1e-6f;
     c.conv = (void*)0x20000; c.state = (float*)0x40000; c.num_slots = 4;
     c.conv_slot_stride = 9 * 256; c.conv_dim_stride = 3; c.conv_pos_stride = 1;
     c.state_slot_stride = 2 * 128 * 128;
     w.conv_width = 3; bad |= kda_prepare(&w, &c, NULL, &h) != KDA_ERR_UNSUPPORTED; w.conv_width = 4;
     w.rounding = 7; bad |= kda_prepare(&w, &c, NULL, &h) != KDA_ERR_SHAPE; w.rounding = 0;
+    w.l2_eps = 0.0f; bad |= kda_prepare(&w, &c, NULL, &h) != KDA_ERR_SHAPE; w.l2_eps = 1e-6f;
+    c.check_distinct = 3; bad |= kda_prepare(&w, &c, NULL, &h) != KDA_ERR_SHAPE; c.check_distinct = 0;
     c.state = (float*)0x40004; bad |= kda_prepare(&w, &c, NULL, &h) != KDA_ERR_ALIGN;
     bad |= h != 0;
     bad |= kda_decode(NULL, (void*)0x1000, 1154, 1, (void*)0x2000, (void*)0x3000, NULL) != KDA_ERR_NULL;

@@ -1,5 +1,7 @@
-"""The C-ABI library loads, exports every function include/kda.h declares, and its
-host-side validation answers without a GPU (no call here reaches the device)."""
+"""The C-ABI library loads, exports every function include/kda.h declares (and the
+measurement library every function include/kda_probe.h declares, the product
+library none of them), and the host-side validation answers without a GPU (no
+call here reaches the device)."""
 import ctypes
 import os
 import re
@@ -12,11 +14,14 @@ HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.j
            if f.endswith(".h")]
 
 import kimi_delta_attention_conv_amd as kda  # noqa: E402
+from kimi_delta_attention_conv_amd import probe as kprobe  # noqa: E402
 
 
-def declared_functions():
+def declared_functions(header=None):
     names = set()
     for path in HEADERS:
+        if header is not None and os.path.basename(path) != header:
+            continue
         text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
         names.update(re.findall(r"^\s*(?:const\s+)?[\w\*\s]+?\b(kda_\w+)\s*\(", text,
                                 flags=re.M))
@@ -30,21 +35,41 @@ def lib():
     return kda.load_library()
 
 
+@pytest.fixture(scope="module")
+def plib():
+    if not os.path.exists(kprobe.LIB_PATH):
+        pytest.skip("libkda_probe.so not built (run __graft_entry__.build())")
+    return kprobe.load_probe_library()
+
+
 def test_header_declares_the_boundary():
-    names = declared_functions()
+    names = declared_functions("kda.h")
     for n in ("kda_prepare", "kda_decode", "kda_verify", "kda_device_errors", "kda_destroy",
-              "kda_status_string", "kda_last_hip_error", "kda_probe_copy", "kda_probe_write",
-              "kda_probe_read", "kda_probe_sink_floats", "kda_probe_state_stream"):
+              "kda_status_string", "kda_last_hip_error", "kda_linear", "kda_in_proj",
+              "kda_o_proj", "kda_linear_workspace_bytes"):
         assert n in names, n
+    probes = declared_functions("kda_probe.h")
+    for n in ("kda_probe_copy", "kda_probe_write", "kda_probe_read", "kda_probe_sink_floats",
+              "kda_probe_state_stream", "kda_probe_copy_runs", "kda_probe_write_runs"):
+        assert n in probes, n
 
 
-def test_every_declared_symbol_is_exported(lib):
-    out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], check=True,
+def _exported(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], check=True,
                          capture_output=True, text=True).stdout
-    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
-    for n in declared_functions():
+    return set(line.split()[-1] for line in out.splitlines() if line.strip())
+
+
+def test_every_declared_symbol_is_exported(lib, plib):
+    exported = _exported(kda.LIB_PATH)
+    for n in declared_functions("kda.h"):
         assert n in exported, f"{n} declared in kda.h but not exported"
         assert getattr(lib, n) is not None
+    probe_exported = _exported(kprobe.LIB_PATH)
+    for n in declared_functions("kda_probe.h"):
+        assert n in probe_exported, f"{n} declared in kda_probe.h but not exported"
+        assert n not in exported, f"{n} (measurement only) exported by the product library"
+        assert getattr(plib, n) is not None
 
 
 def test_status_strings(lib):
@@ -82,6 +107,10 @@ def _caches(**kw):
     (_weights(norm_head_stride=64), _caches(), -2),
     (_weights(norm_eps=float("nan")), _caches(), -2),
     (_weights(l2_eps=-1.0), _caches(), -2),
+    (_weights(l2_eps=0.0), _caches(), -2),
+    (_weights(norm_eps=0.0), _caches(), -2),
+    (_weights(), _caches(check_distinct=2), -2),
+    (_weights(), _caches(check_distinct=-1), -2),
     (_weights(rounding=2), _caches(), -2),
     (_weights(rounding=-1), _caches(), -2),
     (_weights(), _caches(num_slots=0), -2),
@@ -104,7 +133,8 @@ def test_prepare_validation_without_gpu(lib, weights, caches, status):
     assert h.value is None
 
 
-def test_probe_validation_without_gpu(lib):
+def test_probe_validation_without_gpu(plib):
+    lib = plib
     assert lib.kda_probe_copy(None, 0x1000, 16, None) == -1
     assert lib.kda_probe_write(0x1008, 16, 1.0, None) == -3
     assert lib.kda_probe_read(0x1000, 24, 0x2000, None) == -3
@@ -113,11 +143,15 @@ def test_probe_validation_without_gpu(lib):
     assert lib.kda_probe_sink_floats() > 0
 
 
-def test_state_stream_probe_validation_without_gpu(lib):
+def test_state_stream_probe_validation_without_gpu(plib):
+    lib = plib
     fake = 0x10000   # never dereferenced: validation fails before any HIP call
     tile = 128 * 128
     call = lambda state=fake, stride=12 * tile, slots_n=16, slots=fake, rs=8, acc=fake, R=4, L=8, \
-        H=12: lib.kda_probe_state_stream(state, stride, slots_n, slots, rs, acc, R, L, H, None)
+        H=12, opt=0: lib.kda_probe_state_stream(state, stride, slots_n, slots, rs, acc, R, L, H,
+                                                opt, None)
+    assert call(opt=4) == -2
+    assert call(opt=-1) == -2
     assert call(L=0) == -2
     assert call(L=9) == -2
     assert call(H=0) == -2
@@ -197,6 +231,7 @@ def test_headers_are_plain_c_and_a_c_program_links(lib, tmp_path):
         "    if (strcmp(kda_status_string(KDA_OK), \"ok\") != 0) return 3;\n"
         "    if (kda_destroy(h) != KDA_OK) return 4;\n"
         "    if (kda_decode(h, 0, 0, 1, 0, 0, 0) != KDA_ERR_NULL) return 5;\n"
+
         "    return 0;\n}\n")
     exe = tmp_path / "abi"
     libdir = os.path.dirname(kda.LIB_PATH)

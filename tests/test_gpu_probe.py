@@ -4,12 +4,14 @@ kda_probe_state_stream replays the core kernel's state traffic without its
 arithmetic, for the bench's pattern ceiling. Checked here bit for bit on a small
 pool: each request's carried tile, scaled by 0.999f once per token in fp32,
 lands in every destination slot; skipped requests and every other slot stay
-untouched; the decode form scales in place."""
+untouched; the decode form scales in place. Every variant (with and without the
+barrier between loads and stores, with and without the core's residency) writes
+the same."""
 import numpy as np
 import pytest
 import torch
 
-import kimi_delta_attention_conv_amd as kda
+from kimi_delta_attention_conv_amd import probe as kprobe
 
 pytestmark = pytest.mark.gpu
 
@@ -39,11 +41,13 @@ def _expected(pool, table, accepted, tokens, valid):
 
 # (tokens, verify, requests, heads): 15-unit grids take the probe's 16-wave form,
 # 32 x 12 = 384 units with two tokens its 8-wave form (on a 256-CU device)
+@pytest.mark.parametrize("options", [0, 1, 2, 3])
 @pytest.mark.parametrize("tokens,verify,R,H", [(3, True, 5, 3), (8, True, 5, 3), (1, False, 5, 3),
                                                (2, True, 32, 12)])
-def test_state_stream_probe_writes_scaled_carried_tiles(tokens, verify, R, H):
-    print(f"[case] state stream probe tokens={tokens} verify={verify} R={R} H={H}", flush=True)
-    lib = kda.load_library()
+def test_state_stream_probe_writes_scaled_carried_tiles(tokens, verify, R, H, options):
+    print(f"[case] state stream probe tokens={tokens} verify={verify} R={R} H={H} "
+          f"options={options}", flush=True)
+    lib = kprobe.load_probe_library()
     num_slots, cols = (64, 8 if tokens == 8 else 4) if R * 4 <= 64 else (160, 4)
     g = torch.Generator().manual_seed(900 + tokens)
     pool = torch.randn(num_slots, H, TILE, generator=g).numpy().astype(np.float32)
@@ -62,7 +66,7 @@ def test_state_stream_probe_writes_scaled_carried_tiles(tokens, verify, R, H):
     stream = torch.cuda.current_stream().cuda_stream
     rc = lib.kda_probe_state_stream(state.data_ptr(), H * TILE, num_slots, slots.data_ptr(),
                                     table.shape[1], None if acc is None else acc.data_ptr(),
-                                    R, tokens, H, stream)
+                                    R, tokens, H, options, stream)
     assert rc == 0
     torch.cuda.synchronize()
     want = _expected(pool, table, accepted, tokens, valid)

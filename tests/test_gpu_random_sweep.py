@@ -35,7 +35,7 @@ def _core_params(i):
     return dict(R=R, L=L, H=H, verify=verify, block_table_cols=cols,
                 num_slots=rows + int(rng.integers(0, 9)),
                 conv_dim_first=bool(rng.integers(0, 2)), with_bias=bool(rng.integers(0, 2)),
-                extra_pitch=int(rng.choice([0, 2, 64])), per_head_norm=bool(rng.integers(0, 2)),
+                extra_pitch=int(rng.choice([0, 1, 2, 63])), per_head_norm=bool(rng.integers(0, 2)),
                 beta_std=float(rng.choice([1.0, 2.0, 4.0])),
                 a_log_range=[(-1.0, 1.0), (-3.0, 2.0)][int(rng.integers(0, 2))])
 

@@ -170,7 +170,7 @@ def test_host_validation_leaves_device_untouched():
         cases = [
             (lambda: kda.kda_verify(h, p.data_ptr(), case.pitch - 2, 2, 3, slots.data_ptr(), 3,
                                     acc.data_ptr(), o.data_ptr()), -2),
-            (lambda: kda.kda_verify(h, p.data_ptr(), case.pitch + 1, 2, 3, slots.data_ptr(), 3,
+            (lambda: kda.kda_verify(h, p.data_ptr(), case.pitch - 1, 2, 3, slots.data_ptr(), 3,
                                     acc.data_ptr(), o.data_ptr()), -2),
             (lambda: kda.kda_verify(h, p.data_ptr(), case.pitch, 2, 9, slots.data_ptr(), 9,
                                     acc.data_ptr(), o.data_ptr()), -4),
@@ -178,7 +178,7 @@ def test_host_validation_leaves_device_untouched():
                                     acc.data_ptr(), o.data_ptr()), -2),
             (lambda: kda.kda_verify(h, p.data_ptr(), case.pitch, 2, 3, slots.data_ptr(), 3,
                                     0, o.data_ptr()), -1),
-            (lambda: kda.kda_verify(h, p.data_ptr() + 2, case.pitch, 2, 3, slots.data_ptr(), 3,
+            (lambda: kda.kda_verify(h, p.data_ptr() + 1, case.pitch, 2, 3, slots.data_ptr(), 3,
                                     acc.data_ptr(), o.data_ptr()), -3),
             (lambda: kda.kda_decode(h, p.data_ptr(), case.pitch, -1, slots.data_ptr(),
                                     o.data_ptr()), -2),
@@ -317,3 +317,97 @@ def test_eight_and_sixteen_wave_units_agree_bit_exact(L):
     for key in ("out", "conv", "state"):
         assert np.array_equal(whole[key].view(np.uint8), split[key].view(np.uint8)), key
     assert whole["errors"] == split["errors"] == 0
+
+
+@pytest.mark.parametrize("kind", ["across", "within", "decode"])
+def test_distinct_check_skips_colliding_requests(kind):
+    """With check_distinct, every request naming a destination slot that another
+    (request, token) of the call also names is skipped and counted, exactly as the
+    oracle's checked mode defines it; the others are unaffected."""
+    import dataclasses
+
+    from gpu_cases import run_gpu
+    if kind == "decode":
+        base = make_case(R=8, L=1, H=3, num_slots=16, seed=406, verify=False)
+        s = base.slots.clone()
+        s[5] = s[1]
+        involved = {1, 5}
+    else:
+        base = make_case(R=6, L=3, H=2, num_slots=32, seed=407, verify=True)
+        s = base.slots.clone()
+        if kind == "across":
+            s[3, 1] = s[0, 2]
+            involved = {0, 3}
+        else:
+            s[2, 2] = s[2, 0]
+            involved = {2}
+    case = dataclasses.replace(base, slots=s)
+    print(f"[case] distinct check {kind}", flush=True)
+    ref = run_oracle(case, check_distinct=True)
+    assert ref["skipped"] == len(involved)
+    got = run_gpu(case, check_distinct=True)
+    assert_parity(case, ref, got, case.state.numpy(), skip=involved, label=f"distinct_{kind}")
+
+
+def test_distinct_check_resets_between_calls():
+    """The per-slot claims are cleared at the end of every call: a call with a
+    collision, then a call without one on the same handle, skips only in the first
+    (both checked against the oracle's checked mode, chained)."""
+    import dataclasses
+
+    from gpu_cases import GpuCase
+    base = make_case(R=6, L=2, H=2, num_slots=24, seed=409, verify=True)
+    s1 = base.slots.clone()
+    s1[4, 0] = s1[1, 1]
+    first = dataclasses.replace(base, slots=s1)
+    ref1 = run_oracle(first, check_distinct=True)
+    assert ref1["skipped"] == 2
+    g = GpuCase(first, check_distinct=True)
+    try:
+        g.run()
+        h1 = g.host()
+        assert h1["errors"] == 2
+        g.run(slots=base.slots)
+        h2 = g.host()
+        assert h2["errors"] == 0
+    finally:
+        g.close()
+    conv1 = torch.from_numpy(ref1["conv"].view(np.int16)).view(torch.bfloat16)
+    second = dataclasses.replace(base, state=torch.from_numpy(ref1["state"]), conv_storage=conv1)
+    ref2 = run_oracle(second, check_distinct=True)
+    assert ref2["skipped"] == 0
+    # slots untouched by the second call keep the GPU's first-call values
+    assert_parity(second, ref2, h2, h1["state"], label="distinct_second_call")
+
+
+def test_odd_pitch_equals_padded_pitch_bit_exact():
+    """An odd pitch (4D + 128 + H for odd H, rows only 2-byte aligned) and a
+    projected base that is only 2-byte aligned take 2-byte loads of f_a; the results
+    equal those of the same rows padded to an even pitch, bit for bit, and meet the
+    oracle's bars."""
+    import dataclasses
+
+    from gpu_cases import GpuCase
+    case = make_case(R=5, L=3, H=3, num_slots=32, seed=408, verify=True)
+    assert case.pitch % 2 == 1
+    padded = torch.zeros(case.S, case.pitch + 1, dtype=torch.bfloat16)
+    padded[:, :case.pitch] = case.projected
+    even = dataclasses.replace(case, projected=padded, pitch=case.pitch + 1)
+    results = []
+    for c, shift in ((case, 0), (case, 1), (even, 0)):
+        buf = torch.zeros(c.S * c.pitch + 1, dtype=torch.bfloat16, device="cuda")
+        buf[shift: shift + c.S * c.pitch] = c.projected.reshape(-1).cuda()
+        proj = buf[shift: shift + c.S * c.pitch].view(c.S, c.pitch)
+        assert proj.data_ptr() % 4 == 2 * shift
+        print(f"[case] pitch {c.pitch} base offset {2 * shift} B", flush=True)
+        g = GpuCase(c)
+        try:
+            g.run(projected=proj)
+            results.append(g.host())
+        finally:
+            g.close()
+    for k in ("out", "conv", "state"):
+        assert np.array_equal(results[0][k], results[1][k]), k
+        assert np.array_equal(results[0][k], results[2][k]), k
+    ref = run_oracle(case)
+    assert_parity(case, ref, results[0], case.state.numpy(), label="odd_pitch")
