@@ -38,6 +38,8 @@
  *     except for KDA_ERR_HIP (a HIP call failed; see kda_last_hip_error).
  *   - Nothing unwinds across the ABI; no function allocates on the host per
  *     call. Only kda_prepare allocates device memory; kda_destroy frees it.
+ *     kda_linear_noalloc uses a static per-GPU buffer of the library instead
+ *     of a workspace and allocates nothing.
  *   - Within one call every (request, token) must name its own destination
  *     slot ([prepared] run: a block-table slice). A slot named twice races and
  *     has no defined result, unless the caches were registered with
@@ -68,7 +70,9 @@ typedef enum {
     KDA_ERR_UNSUPPORTED = -4, /* valid but not supported: conv width != 4, L > 8 */
     KDA_ERR_HIP = -5,         /* a HIP runtime call failed (kda_last_hip_error names it) */
     KDA_ERR_NOMEM = -6,       /* device or host allocation failed in kda_prepare */
-    KDA_ERR_DEVICE = -7       /* the current HIP device is not the one the handle was prepared on */
+    KDA_ERR_DEVICE = -7,      /* the current HIP device is not the one the handle was prepared on */
+    KDA_ERR_SCRATCH = -8      /* kda_linear_noalloc: the shape needs more scratch than
+                                 KDA_NOALLOC_SCRATCH_BYTES */
 } kda_status;
 
 typedef struct kda_handle_s* kda_handle;
@@ -248,6 +252,27 @@ kda_status kda_linear(const void* x, int64_t x_pitch, const void* w, void* y, in
  * the shape is never split (or the shape is invalid). Host-only. */
 size_t kda_linear_workspace_bytes(int32_t M, int32_t N, int32_t K);
 
+/* Size of the static scratch buffer of kda_linear_noalloc, per GPU. */
+#define KDA_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+
+/* kda_linear for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc): the same
+ * kernels and results as kda_linear given a workspace of
+ * kda_linear_workspace_bytes(M, N, K), with the K split's fp32 partial tiles
+ * in a static device buffer of the library instead (KDA_NOALLOC_SCRATCH_BYTES
+ * per GPU, held from the library's load until the process ends; enough for
+ * in_proj's split up to 256 rows). It calls no allocator. Every call on one
+ * GPU shares that GPU's buffer: calls that overlap in time on one GPU (other
+ * streams or threads) race and must be serialised by the caller (one stream
+ * is enough). Arguments, layouts and errors as kda_linear, plus
+ * KDA_ERR_SCRATCH when kda_linear_workspace_bytes(M, N, K) exceeds
+ * KDA_NOALLOC_SCRATCH_BYTES (nothing is enqueued then). */
+kda_status kda_linear_noalloc(const void* x, int64_t x_pitch, const void* w, void* y,
+                              int64_t y_pitch, int32_t M, int32_t N, int32_t K,
+                              void* hip_stream);
+
+/* KDA_NOALLOC_SCRATCH_BYTES, as the library was built. Host-only. */
+size_t kda_noalloc_scratch_bytes(void);
 
 /* in_proj: N = 4D + 128 + H packed outputs (D = 128 heads), K = hidden;
  * projected rows are `pitch` elements apart (pitch >= N). Workspace as for

@@ -17,6 +17,7 @@ __all__ = [
     "KdaError", "KdaWeights", "KdaCaches", "load_library", "kda_prepare", "kda_decode",
     "kda_verify", "kda_device_errors", "kda_destroy", "kda_status_string", "KdaCore",
     "kda_linear", "kda_linear_workspace_bytes", "kda_in_proj", "kda_o_proj", "linear",
+    "kda_linear_noalloc", "kda_noalloc_scratch_bytes",
     "HEAD_DIM", "FA_RANK", "CONV_WIDTH", "MAX_TOKENS", "ROUNDING",
 ]
 
@@ -30,7 +31,8 @@ ROUNDING = {"fused": 0, "bf16_handoff": 1}
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
 STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_ALIGN",
-          -4: "KDA_ERR_UNSUPPORTED", -5: "KDA_ERR_HIP", -6: "KDA_ERR_NOMEM", -7: "KDA_ERR_DEVICE"}
+          -4: "KDA_ERR_UNSUPPORTED", -5: "KDA_ERR_HIP", -6: "KDA_ERR_NOMEM", -7: "KDA_ERR_DEVICE",
+          -8: "KDA_ERR_SCRATCH"}
 
 
 class KdaError(RuntimeError):
@@ -100,6 +102,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         f.restype = ctypes.c_int
     lib.kda_linear_workspace_bytes.argtypes = [i32, i32, i32]
     lib.kda_linear_workspace_bytes.restype = sz
+    lib.kda_linear_noalloc.argtypes = [vp, i64, vp, vp, i64, i32, i32, i32, vp]
+    lib.kda_linear_noalloc.restype = ctypes.c_int
+    lib.kda_noalloc_scratch_bytes.argtypes = []
+    lib.kda_noalloc_scratch_bytes.restype = sz
     _lib = lib
     return lib
 
@@ -145,6 +151,16 @@ def kda_linear(x: int, x_pitch: int, w: int, y: int, y_pitch: int, M: int, N: in
 
 def kda_linear_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(load_library().kda_linear_workspace_bytes(M, N, K))
+
+
+def kda_linear_noalloc(x: int, x_pitch: int, w: int, y: int, y_pitch: int, M: int, N: int,
+                       K: int, stream: int = 0) -> None:
+    _check(load_library().kda_linear_noalloc(x, x_pitch, w, y, y_pitch, M, N, K, stream),
+           "kda_linear_noalloc")
+
+
+def kda_noalloc_scratch_bytes() -> int:
+    return int(load_library().kda_noalloc_scratch_bytes())
 
 
 def kda_in_proj(x: int, x_pitch: int, w_in: int, projected: int, pitch: int, rows: int,

@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")
 PROBE_LIB = os.path.join(PKG, "libkda_probe.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("kda_core.hip", "kda_linear.hip", "kda_api.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("kda_core.hip", "kda_linear.hip", "kda_api.cpp",
+                                            "kda_noalloc.hip")]
 PROBE_SOURCES = [os.path.join(CSRC, "hbm_probe.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -144,6 +144,7 @@ const char* kda_status_string(kda_status s) {
         case KDA_ERR_HIP: return "a HIP runtime call failed";
         case KDA_ERR_NOMEM: return "out of memory";
         case KDA_ERR_DEVICE: return "the current device is not the handle's device";
+        case KDA_ERR_SCRATCH: return "the shape needs more scratch than the library's static buffer holds";
     }
     return "unknown status";
 }

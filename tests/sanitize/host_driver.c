@@ -27,8 +27,12 @@ int main(void) {
     bad |= kda_linear((void*)0x1000, 64, (void*)0x2000, (void*)0x3000, 16, -1, 16, 64, NULL, 0, NULL) != KDA_ERR_SHAPE;
     bad |= kda_linear((void*)0x1008, 64, (void*)0x2000, (void*)0x3000, 16, 4, 16, 64, NULL, 0, NULL) != KDA_ERR_ALIGN;
     bad |= kda_linear_workspace_bytes(64, 6284, 7168) != 4u * 50 * 64 * 128 * 4;
+    bad |= kda_linear_noalloc((void*)0x1000, 4096, (void*)0x2000, (void*)0x3000, 40000, 256,
+                              40000, 4096, NULL) != KDA_ERR_SCRATCH;
+    bad |= kda_linear_noalloc(NULL, 64, (void*)0x2000, (void*)0x3000, 16, 4, 16, 64, NULL) != KDA_ERR_NULL;
+    bad |= kda_noalloc_scratch_bytes() != KDA_NOALLOC_SCRATCH_BYTES;
     bad |= kda_probe_copy(NULL, (void*)0x1000, 16, NULL) != KDA_ERR_NULL;
-    for (int s = 0; s >= -8; --s) bad |= kda_status_string((kda_status)s) == NULL;
+    for (int s = 0; s >= -9; --s) bad |= kda_status_string((kda_status)s) == NULL;
     bad |= strlen(kda_last_hip_error()) != 0;
     bad |= kda_destroy(NULL) != KDA_OK;
     printf("host validation under sanitizers: %s\n", bad ? "FAIL" : "ok");

@@ -46,7 +46,8 @@ def test_header_declares_the_boundary():
     names = declared_functions("kda.h")
     for n in ("kda_prepare", "kda_decode", "kda_verify", "kda_device_errors", "kda_destroy",
               "kda_status_string", "kda_last_hip_error", "kda_linear", "kda_in_proj",
-              "kda_o_proj", "kda_linear_workspace_bytes"):
+              "kda_o_proj", "kda_linear_workspace_bytes", "kda_linear_noalloc",
+              "kda_noalloc_scratch_bytes"):
         assert n in names, n
     probes = declared_functions("kda_probe.h")
     for n in ("kda_probe_copy", "kda_probe_write", "kda_probe_read", "kda_probe_sink_floats",
@@ -74,7 +75,7 @@ def test_every_declared_symbol_is_exported(lib, plib):
 
 def test_status_strings(lib):
     seen = set()
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         s = kda.kda_status_string(code)
         assert s and s not in seen
         seen.add(s)
@@ -183,6 +184,27 @@ def test_linear_validation_without_gpu(lib):
     assert lib.kda_o_proj(fake, 64, fake, fake, 16, 4, 5000, 64, None, 0, None) == -2
 
 
+def test_noalloc_validation_without_gpu(lib):
+    """kda_linear_noalloc validates like kda_linear and rejects shapes whose K split
+    needs more than the static scratch buffer, all before any HIP call."""
+    fake = 0x10000
+    cap = lib.kda_noalloc_scratch_bytes()
+    assert cap == 32 * 1024 * 1024
+    for M, N, K, status in [(-1, 16, 64, -2), (4, 0, 64, -2), (4, 16, 60, -2),
+                            ((1 << 20) + 1, 16, 64, -2), (1 << 20, 1 << 24, 64, -2)]:
+        assert lib.kda_linear_noalloc(fake, max(K, 8), fake, fake, max(N, 1), M, N, K,
+                                      None) == status, (M, N, K)
+    assert lib.kda_linear_noalloc(None, 64, fake, fake, 16, 4, 16, 64, None) == -1
+    assert lib.kda_linear_noalloc(fake + 8, 64, fake, fake, 16, 4, 16, 64, None) == -3
+    assert lib.kda_linear_noalloc(fake, 64, fake, fake, 16, 0, 16, 64, None) == 0
+    # 256 rows of a 40,000-wide projection split K over 4 x 313 tiles: 164 MB
+    big = lib.kda_linear_workspace_bytes(256, 40000, 4096)
+    assert big > cap
+    assert lib.kda_linear_noalloc(fake, 4096, fake, fake, 40000, 256, 40000, 4096, None) == -8
+    # in_proj up to 256 rows fits
+    assert lib.kda_linear_workspace_bytes(256, 6284, 7168) <= cap
+
+
 def test_linear_workspace_bytes(lib):
     # 33..256 rows, K >= 4096 and a multiple of 256: 4 K slices of fp32 tiles of
     # 64, 128 or 256 rows x 128 columns
@@ -231,7 +253,8 @@ def test_headers_are_plain_c_and_a_c_program_links(lib, tmp_path):
         "    if (strcmp(kda_status_string(KDA_OK), \"ok\") != 0) return 3;\n"
         "    if (kda_destroy(h) != KDA_OK) return 4;\n"
         "    if (kda_decode(h, 0, 0, 1, 0, 0, 0) != KDA_ERR_NULL) return 5;\n"
-
+        "    if (kda_noalloc_scratch_bytes() != KDA_NOALLOC_SCRATCH_BYTES) return 6;\n"
+        "    if (kda_linear_noalloc(0, 64, 0, 0, 16, 4, 16, 64, 0) != KDA_ERR_NULL) return 7;\n"
         "    return 0;\n}\n")
     exe = tmp_path / "abi"
     libdir = os.path.dirname(kda.LIB_PATH)
