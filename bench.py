@@ -80,7 +80,53 @@ def parse_args():
     ap.add_argument("--proj", action="store_true",
                     help="time the in_proj / o_proj projections at the workload's row count "
                          "instead of the core (prints one JSON line)")
+    ap.add_argument("--record-traffic", nargs=3, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV"),
+                    help="(CPU only) record the core kernel's HBM bytes per launch for WORKLOAD "
+                         "from two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE; each run also "
+                         "timing the 1 GiB copy probe that calibrates the counters) into "
+                         "profiles/kda_core_traffic.json with the current kernel source digest")
     return ap.parse_args()
+
+
+def counter_means(csv_path, counter):
+    """Mean value per dispatch of `counter` for the core kernel and the 1 GiB
+    grid-stride copy probe, from a rocprofv3 counter-collection CSV."""
+    import csv
+    sums = {}
+    for row in csv.DictReader(open(csv_path)):
+        if row.get("Counter_Name") != counter:
+            continue
+        name = row.get("Kernel_Name", "")
+        key = "core" if "kda_core_kernel" in name else "copy" if "probe_copy(" in name or \
+            name.split("(")[0].endswith("probe_copy") else None
+        if key is None:
+            continue
+        v = float(row["Counter_Value"])
+        n, tot = sums.get(key, (0, 0.0))
+        sums[key] = (n + 1, tot + v)
+    if "core" not in sums or "copy" not in sums:
+        raise SystemExit(f"{csv_path}: no {counter} rows for both the core kernel and probe_copy")
+    return {k: (tot / n, n) for k, (n, tot) in sums.items()}
+
+
+def record_traffic(workload, fetch_csv, write_csv):
+    """HBM bytes a launch: each counter (KiB a dispatch) scaled by what it reads
+    for the copy probe, which moves exactly 1 GiB each way."""
+    f = counter_means(fetch_csv, "FETCH_SIZE")
+    w = counter_means(write_csv, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+    fetch_scale = gib_kib / f["copy"][0]
+    write_scale = gib_kib / w["copy"][0]
+    read_bytes = f["core"][0] * fetch_scale * 1024
+    write_bytes = w["core"][0] * write_scale * 1024
+    rec = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
+    rec[workload] = {"source_digest": source_digest(), "fetch_size_kib": round(f["core"][0], 1),
+                     "write_size_kib": round(w["core"][0], 1), "dispatches": [f["core"][1], w["core"][1]],
+                     "fetch_scale": round(fetch_scale, 5), "write_scale": round(write_scale, 5),
+                     "read_bytes": int(read_bytes), "write_bytes": int(write_bytes),
+                     "bytes_per_launch": int(read_bytes + write_bytes)}
+    json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps({workload: rec[workload]}))
 
 
 def source_digest() -> str:
@@ -529,6 +575,9 @@ def cpu_baseline(case, seconds):
 
 def main():
     args = parse_args()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the library "
               "has no multi-GPU path: the core shards by heads and requests with no exchange, "
