@@ -316,6 +316,7 @@ kda_status kda_linear(const void* x, int64_t x_pitch, const void* w, void* y, in
     p.K = K;
     p.part = static_cast<float*>(workspace);
     p.part_floats = workspace == nullptr ? 0 : (int64_t)(workspace_bytes / sizeof(float));
+    p.cu_count = kda::current_device_cus();
     hipError_t e = kda::launch_linear(p, static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? KDA_OK : hip_fail(e, "kda_linear launch");
 }

@@ -78,6 +78,7 @@ struct LinearParams {
     int32_t M, N, K;     // K a multiple of 8
     float* part;         // fp32 workspace for a K split, or null
     int64_t part_floats; // its capacity in floats
+    int32_t cu_count;    // compute units of the current device (0: unknown)
 };
 
 hipError_t launch_prepare(const PrepareParams& in, const PreparedWeights& out, hipStream_t s);
@@ -89,6 +90,8 @@ hipError_t launch_zero(int32_t* p, int64_t n, hipStream_t s);
 // rules (slots in range, accepted count in 1 .. L).
 hipError_t launch_claims(int tokens, const CoreParams& p, int32_t* claims, bool clear, hipStream_t s);
 hipError_t launch_linear(const LinearParams& p, hipStream_t s);
+// Compute units of the current device, read once per device (0 if the query fails).
+int32_t current_device_cus();
 // Workspace floats launch_linear uses for a K split of this shape (0: none).
 int64_t linear_workspace_floats(int32_t M, int32_t N, int32_t K);
 hipError_t launch_core(int tokens, const CoreParams& p, hipStream_t s);

@@ -26,7 +26,10 @@
 // BN tiles, X and W blocks loaded straight into a ring of LDS stages; with a
 // caller's workspace and a long K (33 to 256 rows) the same kernel splits K
 // over 4 slices of workgroups and linear_split_sum adds the fp32 slices in
-// slice order. Tiled (M > 64, other K): 128 x 64 tiles staged through
+// slice order. Pipelined (above 256 rows, K >= 4096, tiles filling three
+// quarters to all but one of the CUs): the same tiles and arithmetic with the
+// fragment reads overlapping the MFMAs and the idle CUs prefetching the tiles'
+// lines into L2. Tiled (M > 64, other K): 128 x 64 tiles staged through
 // registers.
 #include "kda_internal.h"
 
@@ -338,9 +341,9 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void linear_lds_kernel(const L
     }
     const int nkb = kc / (64 * SUB);             // stages of K (the launch checks K % (64 SUB SPLIT))
     auto issue = [&](int kb) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the builtin's LDS operand has no host type
         const int st = kb % STAGES;
         const int kk = min(kb, nkb - 1) * 64 * SUB;     // past the end: a harmless re-read
-#if defined(__HIP_DEVICE_COMPILE__)   // the builtin's LDS operand has no host type
 #pragma unroll
         for (int j = 0; j < LPB; ++j)
 #pragma unroll
@@ -494,6 +497,248 @@ hipError_t launch_lds(const LinearParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Pipelined direct-to-LDS kernel with prefetching workgroups, for shapes
+// whose 128 x 128 tiles fill three quarters to all but one of the CUs (above
+// 256 rows with a K of at least 4096: in_proj at 512 rows makes 200 tiles for
+// 256 CUs). It repeats linear_lds_kernel<128, 128, *, 2, 4, 2>'s arithmetic bit
+// for bit (same tiles, waves, K halves and summation order) with two changes:
+//
+// * Software pipelining of the fragments: after the barrier that publishes
+//   block kb + 1, each wave reads block kb + 1's fragments and only then issues
+//   block kb's MFMAs, on fragments read one step earlier, so the LDS reads that
+//   follow every barrier overlap matrix work. The slot of block kb - 1, whose
+//   fragments every wave has consumed before reaching that barrier, takes block
+//   kb + STAGES - 1. The direct loads use the buffer (MUBUF) form: while a
+//   FLAT-encoded global_load_lds is in flight, the compiler's wait-count pass
+//   waits for every LDS read before any fragment is used, which undoes the
+//   overlap. Byte offsets are 32-bit (the dispatch checks both matrices fit).
+// * Prefetching workgroups: those launched past the tiles run on CUs the tiles
+//   leave idle and load, K block by K block, a share of the X and W lines that
+//   the tiles of their XCD are about to read (into a private LDS scratch; never
+//   waited for until they exit), so that the tiles' own loads find those lines
+//   in L2. Measured on MI355X: a copy of this kernel without its MFMAs moves
+//   the tiles' data at ~50 GB/s a CU when every CU of an XCD misses on the same
+//   lines (66 us at 512 rows, against 70 us with the MFMAs); with the
+//   prefetching workgroups the full kernel takes 58 us. With many more idle CUs
+//   (384 rows: 150 tiles, 106 prefetching workgroups) they run far ahead of the
+//   tiles and evict lines before use, which was slower: hence the three-quarter
+//   rule in the dispatch.
+
+// Share of one XCD's upcoming X and W lines for a prefetching workgroup (tile t
+// runs on XCD t / (tiles / 8) in the XCD-blocked order of the tile kernels).
+template <int BN, int THREADS>
+__device__ __forceinline__ void prefetch_share(const LinearParams& p, int tiles, int mblocks, uint16_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int q = tiles >> 3;
+    if (q == 0) return;
+    const int x = blockIdx.x & 7;                       // this workgroup's XCD
+    const int extra = (int)gridDim.x - tiles;
+    const int v0 = ((x - tiles) % 8 + 8) % 8;           // first prefetching workgroup on XCD x
+    const int npf = (extra - v0 + 7) / 8;               // prefetching workgroups on XCD x
+    const int jpf = ((int)blockIdx.x - tiles) / 8;
+    const int n_lo = (x * q / mblocks) * BN;
+    const int n_hi = min(p.N, ((x * q + q - 1) / mblocks + 1) * BN);
+    const int rows = p.M + (n_hi - n_lo);               // X rows, then the XCD's W rows
+    const int nk = p.K / 64;
+    const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    // a thread takes whole rows and walks them in K order, so each wave touches
+    // its rows' lines block by block
+    for (int r = jpf + npf * (int)threadIdx.x; r < rows; r += npf * THREADS) {
+        const uint16_t* rp = r < p.M ? p.X + (int64_t)r * p.x_pitch : p.W + (int64_t)(n_lo + r - p.M) * p.K;
+        for (int kb = 0; kb < nk; ++kb)   // one 4-byte load a 128-byte line
+            __builtin_amdgcn_global_load_lds(rp + kb * 64, lds + wv * 128, 4, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // no direct load may still target LDS at exit
+#endif
+}
+
+template <int BM, int BN, int STAGES, int WGM, int WGN, int KS>
+__global__ __launch_bounds__(64 * WGM * WGN * KS) void linear_pipe_kernel(const LinearParams p) {
+    static_assert(KS == 1 || KS == 2, "K split of a 64-wide block into 1 or 2 parts");
+    static_assert(STAGES >= 3, "a slot being filled, one being read, one consumed");
+    constexpr int WAVES = WGM * WGN * KS;
+    constexpr int ROWS = BM + BN;
+    constexpr int LPB = ROWS / (8 * WAVES);           // direct loads per thread per K block
+    constexpr int TM = BM / WGM / 16, TN = BN / WGN / 16;
+    constexpr int SPW = 2 / KS;                       // 32-wide K steps a wave takes per block
+    static_assert(LPB * 8 * WAVES == ROWS, "rows must split into whole wave loads");
+    static_assert((BM / 8) % WAVES == 0, "a wave load lies wholly in X or in W");
+    __shared__ __attribute__((aligned(1024))) uint16_t sm[STAGES][ROWS * 64];
+
+    const int mblocks = (p.M + BM - 1) / BM;
+    const int tiles = mblocks * ((p.N + BN - 1) / BN);
+    if ((int)blockIdx.x >= tiles) {
+        prefetch_share<BN, 64 * WAVES>(p, tiles, mblocks, &sm[0][0]);
+        return;
+    }
+    int t = blockIdx.x;
+    {
+        const int q = tiles >> 3;
+        if ((int)blockIdx.x < 8 * q) t = (blockIdx.x & 7) * q + (blockIdx.x >> 3);
+    }
+    const int m0 = (t % mblocks) * BM;
+    const int n0 = (t / mblocks) * BN;
+    // the wave index in a scalar register: the direct loads' LDS address (M0)
+    // is then provably uniform, with no per-lane loop around each load
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int kh = wave / (WGM * WGN);
+    const int slot = wave % (WGM * WGN);
+    const int wm = slot / WGN, wn = slot % WGN;
+    const int mn = lane & 15, kg = lane >> 4;
+
+    // byte offset of this lane's 16 bytes of load j of a block (the layout of
+    // linear_lds_kernel: row 8 (WAVES j + wave) + (lane >> 3) of [X rows; W rows],
+    // chunk (lane & 7) ^ (lane >> 3))
+    uint32_t voff[LPB];
+#pragma unroll
+    for (int j = 0; j < LPB; ++j) {
+        const int row = 8 * (WAVES * j + wave) + (lane >> 3);
+        const int chunk = (lane & 7) ^ (lane >> 3);
+        voff[j] = (uint32_t)(row < BM ? (int64_t)min(m0 + row, p.M - 1) * p.x_pitch
+                                      : (int64_t)min(n0 + row - BM, p.N - 1) * p.K) * 2u + 16u * chunk;
+    }
+    const int nkb = p.K / 64;
+#if defined(__HIP_DEVICE_COMPILE__)
+    // no range check in the descriptors: every offset is clamped into its matrix
+    // (an extent computed here made the compiler treat them as per-lane values)
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)p.X, (short)0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)p.W, (short)0, -1, 0x00020000);
+#endif
+    auto issue = [&](int kb) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        const int st = kb % STAGES;
+        const uint32_t kk = (uint32_t)min(kb, nkb - 1) * 128u;   // past the end: a harmless re-read
+#pragma unroll
+        for (int j = 0; j < LPB; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                (WAVES * j < BM / 8) ? rx : rw,
+                (__attribute__((address_space(3))) void*)&sm[st][8 * (WAVES * j + wave) * 64], 16,
+                voff[j] + kk, 0, 0, 0);
+#endif
+    };
+    auto read = [&](int kb, bf16x8 (&a)[SPW][TM], bf16x8 (&b)[SPW][TN]) {
+        const uint16_t* st = sm[kb % STAGES];
+#pragma unroll
+        for (int ss = 0; ss < SPW; ++ss) {
+            const int s = kh * SPW + ss;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = wm * (BM / WGM) + 16 * i + mn;
+                const int pos = (4 * s + kg) ^ (row & 7);
+                a[ss][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + row * 64 + 8 * pos));
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int row = BM + wn * (BN / WGN) + 16 * j + mn;
+                const int pos = (4 * s + kg) ^ (row & 7);
+                b[ss][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + row * 64 + 8 * pos));
+            }
+        }
+    };
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    auto mma = [&](const bf16x8 (&a)[SPW][TM], const bf16x8 (&b)[SPW][TN]) {
+#pragma unroll
+        for (int ss = 0; ss < SPW; ++ss)
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ss][i], b[ss][j], acc[i][j], 0, 0, 0);
+    };
+    // vmcnt: block kb + 1 has landed once at most STAGES - 3 later blocks of this
+    // wave's loads are outstanding (STAGES - 2 before the loop); lgkmcnt: the
+    // fragments of block kb were read one step earlier, so only this step's
+    // NR reads may still be in flight
+    constexpr int NW = (STAGES - 3) * LPB, N0 = (STAGES - 2) * LPB, NR = SPW * (TM + TN);
+    static_assert(N0 < 64 && NR < 16, "the vmcnt field holds 6 bits, lgkmcnt 4");
+    auto step = [&](int kb, const bf16x8 (&ca)[SPW][TM], const bf16x8 (&cb)[SPW][TN],
+                    bf16x8 (&na)[SPW][TM], bf16x8 (&nb)[SPW][TN]) {
+        // unconditional, so that no control-flow join makes the compiler wait
+        // for these reads before the MFMAs: in the last step, block kb + 1 is a
+        // landed copy of the last block, read and never used
+        __builtin_amdgcn_s_waitcnt((NW & 15) | ((NW >> 4) << 14) | (7 << 4) | (15 << 8));
+        __asm__ volatile("s_barrier" ::: "memory");
+        issue(kb + STAGES - 1);
+        read(kb + 1, na, nb);
+        __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (NR << 8));
+        __builtin_amdgcn_sched_barrier(0);
+        mma(ca, cb);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) issue(s);
+    __builtin_amdgcn_s_waitcnt((N0 & 15) | ((N0 >> 4) << 14) | (7 << 4) | (15 << 8));
+    __asm__ volatile("s_barrier" ::: "memory");
+    bf16x8 a0[SPW][TM], b0[SPW][TN], a1[SPW][TM], b1[SPW][TN];
+    read(0, a0, b0);
+    // settle the prologue's LDS and scalar loads here, so that the loop header's
+    // wait state holds only fragment reads
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+    int kb = 0;
+    for (; kb + 2 <= nkb; kb += 2) {
+        step(kb, a0, b0, a1, b1);
+        step(kb + 1, a1, b1, a0, b0);
+    }
+    if (kb < nkb) step(kb, a0, b0, a1, b1);
+    __builtin_amdgcn_s_waitcnt(0);   // no direct load may still target LDS at exit
+
+    if (KS == 2) {   // group 1 parks its tiles in the (now idle) stages, group 0 adds them
+        static_assert(KS == 1 || WGM * WGN * TM * TN * 256 * 4 <= (int)sizeof(sm), "room to reduce");
+        float* red = reinterpret_cast<float*>(&sm[0][0]);
+        __syncthreads();
+        if (kh == 1) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        red[((slot * TM + i) * TN + j) * 256 + r * 64 + lane] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (kh == 1) return;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[i][j][r] += red[((slot * TM + i) * TN + j) * 256 + r * 64 + lane];
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = n0 + wn * (BN / WGN) + 16 * j + mn;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + wm * (BM / WGM) + 16 * i + 4 * kg + r;
+                if (m < p.M && n < p.N) p.Y[(int64_t)m * p.y_pitch + n] = to_bf16(acc[i][j][r]);
+            }
+        }
+}
+
+// 128 x 128 tiles of 2 x 4 waves per K half, 4 stages (128 KB of LDS), and as
+// many prefetching workgroups as the tiles leave CUs idle.
+bool pipe_shape(const LinearParams& p) {
+    const int64_t tiles = (int64_t)((p.N + 127) / 128) * ((p.M + 127) / 128);
+    return p.M > 256 && p.K >= 4096 && p.K % 64 == 0 && p.cu_count > 0 && tiles < p.cu_count &&
+           4 * tiles >= 3 * (int64_t)p.cu_count && (int64_t)p.M * p.x_pitch * 2 <= INT32_MAX &&
+           (int64_t)p.N * p.K * 2 <= INT32_MAX;
+}
+
+hipError_t launch_pipe(const LinearParams& p, hipStream_t s) {
+    // one workgroup a CU: the tiles first, then the prefetching workgroups
+    hipLaunchKernelGGL((linear_pipe_kernel<128, 128, 4, 2, 4, 2>), dim3((unsigned)p.cu_count), dim3(1024), 0, s,
+                       p);
+    return hipGetLastError();
+}
+
 template <int MT, int NT, int WAVES>
 hipError_t launch_skinny(const LinearParams& p, hipStream_t s) {
     const dim3 grid((unsigned)((p.N + 16 * NT - 1) / (16 * NT)), (unsigned)((p.M + 16 * MT - 1) / (16 * MT)));
@@ -551,6 +796,7 @@ hipError_t launch_linear(const LinearParams& p, hipStream_t s) {
         if (p.M <= 128) return launch_lds<128, 128, 3, 2, 4, 2, 1, kSplit>(p, s);
         return launch_lds<256, 128, 3, 4, 2, 2, 1, kSplit>(p, s);
     }
+    if (pipe_shape(p)) return launch_pipe(p, s);
     if (p.K % 128 == 0 && p.M <= 64) {
         if (p.M <= 16) return launch_lds<16, 32, 6, 1, 1, 2, 2>(p, s);
         if (p.M <= 32) return launch_lds<32, 32, 4, 1, 1, 2, 2>(p, s);
@@ -567,6 +813,19 @@ hipError_t launch_linear(const LinearParams& p, hipStream_t s) {
     if (p.M <= 32) return launch_skinny<2, 2, 8>(p, s);
     if (p.M <= 64) return launch_skinny<4, 2, 8>(p, s);
     return launch_tiled<128, 64, 2>(p, s);
+}
+
+int32_t current_device_cus() {
+    static int32_t cus[64] = {};   // per device; a race only writes the same value twice
+    int d = -1;
+    if (hipGetDevice(&d) != hipSuccess || d < 0) return 0;
+    if (d >= 64) return 0;
+    if (cus[d] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess) return 0;
+        cus[d] = n;
+    }
+    return cus[d];
 }
 
 }  // namespace kda

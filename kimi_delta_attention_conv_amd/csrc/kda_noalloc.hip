@@ -80,6 +80,7 @@ kda_status kda_linear_noalloc(const void* x, int64_t x_pitch, const void* w, voi
     p.M = M;
     p.N = N;
     p.K = K;
+    p.cu_count = kda::current_device_cus();
     if (need > 0) {
         int device = -1;
         hipError_t e = hipGetDevice(&device);

@@ -192,3 +192,38 @@ def test_torch_helper_matches_the_abi_call():
     assert np.array_equal(got_plain, direct_plain)
     with pytest.raises(ValueError):
         kda.linear(x.cuda(), w.cuda(), workspace="bogus")
+
+
+def _pipe_class(M, N, K):
+    """Whether kda_linear takes the pipelined kernel with prefetching workgroups:
+    above 256 rows, K >= 4096 (a multiple of 64), 128 x 128 tiles filling three
+    quarters to all but one of the device's compute units."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = -(-M // 128) * -(-N // 128)
+    return M > 256 and K >= 4096 and K % 64 == 0 and tiles < cus and 4 * tiles >= 3 * cus
+
+
+@pytest.mark.parametrize("M,N,K", [(449, 6200, 4096), (500, 6300, 4160), (385, 6144, 4096)])
+def test_pipelined_prefetch_shapes(M, N, K):
+    """Ragged shapes of the pipelined kernel (an odd K-block count among them):
+    every output against the oracle's bar, columns past N untouched, and bit for
+    bit the same as the same product computed in two halves of N, each of which
+    has too few tiles for that kernel and runs the plain 128 x 128 tile kernel
+    with the same summation order."""
+    if not _pipe_class(M, N, K):
+        pytest.skip("the device's compute-unit count puts this shape outside the pipelined class")
+    x, w = make_linear(M, N, K, seed=M + N + K, x_pitch=K + 8)
+    got = _run(x, w, y_pitch=N + 3)
+    assert np.all(got[:, N:] == SENT), "columns beyond N were written"
+    got = got[:, :N]
+    rng = np.random.default_rng(M)
+    ms, ns = rng.integers(0, M, 6000), rng.integers(0, N, 6000)
+    ms[:3], ns[:3] = [M - 1, 0, M - 1], [N - 1, N - 1, 0]
+    _check(x, w, got, ms, ns, label=f"pipelined M={M} N={N} K={K}")
+    h = N // 2
+    assert not _pipe_class(M, h, K) and not _pipe_class(M, N - h, K)
+    lo = _run(x, w[:h].contiguous())
+    hi = _run(x, w[h:].contiguous())
+    assert np.array_equal(got, np.concatenate([lo, hi], axis=1)), "differs from the plain tile kernel"
+    again = _run(x, w, y_pitch=N + 3)
+    assert np.array_equal(got, again[:, :N]), "not deterministic"
