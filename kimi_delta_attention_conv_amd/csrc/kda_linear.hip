@@ -515,14 +515,15 @@ hipError_t launch_lds(const LinearParams& p, hipStream_t s) {
 // * Prefetching workgroups: those launched past the tiles run on CUs the tiles
 //   leave idle and load, K block by K block, a share of the X and W lines that
 //   the tiles of their XCD are about to read (into a private LDS scratch; never
-//   waited for until they exit), so that the tiles' own loads find those lines
-//   in L2. Measured on MI355X: a copy of this kernel without its MFMAs moves
-//   the tiles' data at ~50 GB/s a CU when every CU of an XCD misses on the same
-//   lines (66 us at 512 rows, against 70 us with the MFMAs); with the
-//   prefetching workgroups the full kernel takes 58 us. With many more idle CUs
-//   (384 rows: 150 tiles, 106 prefetching workgroups) they run far ahead of the
-//   tiles and evict lines before use, which was slower: hence the three-quarter
-//   rule in the dispatch.
+//   waited for until they exit), so that the tiles' own loads can find those
+//   lines in L2. Measured on MI355X at 512 rows, where the kernel is bound by
+//   how fast the tiles' data reaches the CUs (a copy without its MFMAs takes as
+//   long): on some boxes of the pool the plain 128 x 128 kernel took 65-71 us
+//   and its data path alone 66 us, and the prefetching workgroups brought both
+//   to 56-59 us; on others every variant took 57-58 us. With many more idle
+//   CUs (384 rows: 150 tiles, 106 prefetching workgroups) they ran far ahead of
+//   the tiles and evicted lines before use, which was slower: hence the
+//   three-quarter rule in the dispatch.
 
 // Share of one XCD's upcoming X and W lines for a prefetching workgroup (tile t
 // runs on XCD t / (tiles / 8) in the XCD-blocked order of the tile kernels).
