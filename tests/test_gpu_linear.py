@@ -227,3 +227,45 @@ def test_pipelined_prefetch_shapes(M, N, K):
     assert np.array_equal(got, np.concatenate([lo, hi], axis=1)), "differs from the plain tile kernel"
     again = _run(x, w, y_pitch=N + 3)
     assert np.array_equal(got, again[:, :N]), "not deterministic"
+
+
+def test_pipelined_prefetch_graph_replays_equal_eager():
+    """The pipelined kernel with prefetching workgroups at in_proj's 512-row shape,
+    captured in a HIP graph once and replayed with three different inputs (eager work
+    between the replays): every replay equals the eager call bit for bit."""
+    import kimi_delta_attention_conv_amd as kda
+    heads = 12
+    M, N, K = 512, 4 * 128 * heads + 128 + heads, HIDDEN
+    if not _pipe_class(M, N, K):
+        pytest.skip("the device's compute-unit count puts this shape outside the pipelined class")
+    _, w = make_linear(1, N, K, seed=901)
+    wd = w.cuda()
+    gen = torch.Generator().manual_seed(902)
+    inputs = [torch.randn(M, K, generator=gen).to(torch.bfloat16) for _ in range(3)]
+    x = torch.zeros(M, K, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(M, N, dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        kda.kda_linear(x.data_ptr(), K, wd.data_ptr(), y.data_ptr(), N, M, N, K,
+                       stream=torch.cuda.current_stream().cuda_stream)
+
+    ref = []
+    for xi in inputs:
+        x.copy_(xi)
+        call()
+        torch.cuda.synchronize()
+        ref.append(y.cpu().view(torch.int16).clone())
+    y.zero_()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for k, xi in enumerate(inputs):
+        x.copy_(xi)
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.cpu().view(torch.int16), ref[k]), f"replay {k}"
+    print("[linear] pipelined 512-row in_proj: 3 graph replays equal eager", flush=True)
