@@ -494,7 +494,7 @@ hipError_t launch_claims_t(const CoreParams& p, int32_t* claims, bool clear, hip
     return hipGetLastError();
 }
 
-// Waves a unit (measured on MI355X, same box, alternating runs): sixteen 8-row
+// Waves a unit (measured on MI355X, one device, alternating runs): sixteen 8-row
 // waves for every one-token call (in-place decode: 73.8 against 77.5 us for
 // 256 requests x 12 heads, 21.4 against 22.6 for 64, although only one such
 // workgroup fits a CU) and for grids of at most one unit a CU, where a unit's

@@ -518,9 +518,9 @@ hipError_t launch_lds(const LinearParams& p, hipStream_t s) {
 //   waited for until they exit), so that the tiles' own loads can find those
 //   lines in L2. Measured on MI355X at 512 rows, where the kernel is bound by
 //   how fast the tiles' data reaches the CUs (a copy without its MFMAs takes as
-//   long): on some boxes of the pool the plain 128 x 128 kernel took 65-71 us
-//   and its data path alone 66 us, and the prefetching workgroups brought both
-//   to 56-59 us; on others every variant took 57-58 us. With many more idle
+//   long): on some devices the plain 128 x 128 kernel took 65-71 us and its
+//   data path alone 66 us, and the prefetching workgroups brought both to
+//   56-59 us; on others every variant took 57-58 us. With many more idle
 //   CUs (384 rows: 150 tiles, 106 prefetching workgroups) they ran far ahead of
 //   the tiles and evicted lines before use, which was slower: hence the
 //   three-quarter rule in the dispatch.
