@@ -33,6 +33,8 @@
 // registers.
 #include "kda_internal.h"
 
+#include <atomic>
+
 namespace kda {
 namespace {
 
@@ -788,9 +790,12 @@ hipError_t launch_linear(const LinearParams& p, hipStream_t s) {
     // stages), one wave or wave pair on each 32-wide K half of a block. Above
     // 64 rows (K a multiple of 64): 128 x 64 tiles of 4 x 2 waves with 4 stages
     // up to 256 rows; 128 x 128 tiles of 2 x 4 waves per K half (16 waves) with
-    // 3 stages beyond. K a multiple of 64 only: one K block a stage up to 64
-    // rows (the skinny kernel up to 16). Other K: the skinny kernel up to 64
-    // rows and the register-staged kernel above.
+    // 3 stages beyond, in the pipelined kernel with 4 stages and prefetching
+    // workgroups on the idle CUs when K >= 4096 and those tiles fill three
+    // quarters to all but one of the CUs (in_proj at 385 to 512 rows). K a
+    // multiple of 64 only: one K block a stage up to 64 rows (the skinny kernel
+    // up to 16). Other K: the skinny kernel up to 64 rows and the
+    // register-staged kernel above.
     if (split_shape(p.M, p.K) && p.part != nullptr &&
         p.part_floats >= linear_workspace_floats(p.M, p.N, p.K)) {
         if (p.M <= 64) return launch_lds<64, 128, 4, 2, 2, 2, 1, kSplit>(p, s);
@@ -817,16 +822,17 @@ hipError_t launch_linear(const LinearParams& p, hipStream_t s) {
 }
 
 int32_t current_device_cus() {
-    static int32_t cus[64] = {};   // per device; a race only writes the same value twice
+    static std::atomic<int32_t> cus[64] = {};   // per device, 0 until first read
     int d = -1;
-    if (hipGetDevice(&d) != hipSuccess || d < 0) return 0;
-    if (d >= 64) return 0;
-    if (cus[d] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess) return 0;
-        cus[d] = n;
+    if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) return 0;
+    int32_t n = cus[d].load(std::memory_order_relaxed);
+    if (n == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess) return 0;
+        n = v;
+        cus[d].store(n, std::memory_order_relaxed);
     }
-    return cus[d];
+    return n;
 }
 
 }  // namespace kda
