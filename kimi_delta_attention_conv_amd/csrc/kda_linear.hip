@@ -515,20 +515,21 @@ hipError_t launch_lds(const LinearParams& p, hipStream_t s) {
 //   waits for every LDS read before any fragment is used, which undoes the
 //   overlap. Byte offsets are 32-bit (the dispatch checks both matrices fit).
 // * Prefetching workgroups: those launched past the tiles run on CUs the tiles
-//   leave idle and load, K block by K block, a share of the X and W lines that
-//   the tiles of their XCD are about to read (into a private LDS scratch; never
-//   waited for until they exit), so that the tiles' own loads can find those
-//   lines in L2. Measured on MI355X at 512 rows, where the kernel is bound by
-//   how fast the tiles' data reaches the CUs (a copy without its MFMAs takes as
-//   long): on some devices the plain 128 x 128 kernel took 65-71 us and its
-//   data path alone 66 us, and the prefetching workgroups brought both to
-//   56-59 us; on others every variant took 57-58 us. With many more idle
-//   CUs (384 rows: 150 tiles, 106 prefetching workgroups) they ran far ahead of
-//   the tiles and evicted lines before use, which was slower: hence the
-//   three-quarter rule in the dispatch.
+//   leave idle and load, K block by K block, a share of the W lines that the
+//   tiles of their XCD are about to read (into a private LDS scratch; never
+//   waited for until they exit), so that the tiles' own loads find those lines
+//   in L2 or the Infinity Cache rather than in HBM. Measured on MI355X at 512
+//   rows, the weight stream is what bounds the kernel: with W lines resident in
+//   L2 a timing copy takes 46.8 us, with X lines resident instead 66.9 us, as
+//   long as with neither (66 us). The prefetching workgroups bring the kernel
+//   from 66 to 53-54 us; prefetching the X lines as well (shared by every column
+//   block of an XCD, and cheap for the tiles) cost 4 us of that. With many more
+//   idle CUs (384 rows: 150 tiles, 106 prefetching workgroups) prefetching ran
+//   far ahead of the tiles and evicted lines before use, which was slower:
+//   hence the three-quarter rule in the dispatch.
 
-// Share of one XCD's upcoming X and W lines for a prefetching workgroup (tile t
-// runs on XCD t / (tiles / 8) in the XCD-blocked order of the tile kernels).
+// Share of one XCD's upcoming W lines for a prefetching workgroup (tile t runs
+// on XCD t / (tiles / 8) in the XCD-blocked order of the tile kernels).
 template <int BN, int THREADS>
 __device__ __forceinline__ void prefetch_share(const LinearParams& p, int tiles, int mblocks, uint16_t* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -541,13 +542,13 @@ __device__ __forceinline__ void prefetch_share(const LinearParams& p, int tiles,
     const int jpf = ((int)blockIdx.x - tiles) / 8;
     const int n_lo = (x * q / mblocks) * BN;
     const int n_hi = min(p.N, ((x * q + q - 1) / mblocks + 1) * BN);
-    const int rows = p.M + (n_hi - n_lo);               // X rows, then the XCD's W rows
+    const int rows = n_hi - n_lo;                       // the XCD's W rows
     const int nk = p.K / 64;
     const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     // a thread takes whole rows and walks them in K order, so each wave touches
     // its rows' lines block by block
     for (int r = jpf + npf * (int)threadIdx.x; r < rows; r += npf * THREADS) {
-        const uint16_t* rp = r < p.M ? p.X + (int64_t)r * p.x_pitch : p.W + (int64_t)(n_lo + r - p.M) * p.K;
+        const uint16_t* rp = p.W + (int64_t)(n_lo + r) * p.K;
         for (int kb = 0; kb < nk; ++kb)   // one 4-byte load a 128-byte line
             __builtin_amdgcn_global_load_lds(rp + kb * 64, lds + wv * 128, 4, 0, 0);
     }
