@@ -404,7 +404,9 @@ def bench_projections(args, torch, kda):
 def bench_layer(args, torch, kda):
     """One layer's attention-core step as a serving loop runs it: in_proj
     (hidden 7168 -> packed row), the core (decode or verify), o_proj (D -> 7168).
-    Weight copies and slot sets rotate so that every step streams from HBM."""
+    Weight copies and slot sets rotate so that every step streams from HBM: each
+    weight has enough copies (at least 600 MiB of them) that a kernel timed
+    alone does not find its weights in the 256 MB Infinity Cache either."""
     from kda_inputs import HIDDEN, make_linear
     w = Workload(torch, kda, args.config)
     case = w.case
@@ -414,10 +416,11 @@ def bench_layer(args, torch, kda):
     dev = "cuda"
     x, w_in = make_linear(S, n_in, HIDDEN, seed=21)
     _, w_o = make_linear(1, HIDDEN, D, seed=22)
-    copies = 4
+    in_copies = max(4, -(-(600 << 20) // (n_in * HIDDEN * 2)))
+    o_copies = max(4, -(-(600 << 20) // (HIDDEN * D * 2)))
     xs = x.to(dev)
-    w_ins = [w_in.to(dev) for _ in range(copies)]
-    w_os = [w_o.to(dev) for _ in range(copies)]
+    w_ins = [w_in.to(dev) for _ in range(in_copies)]
+    w_os = [w_o.to(dev) for _ in range(o_copies)]
     projected = w.projected
     core_out = w.out
     out = torch.empty(S, HIDDEN, dtype=torch.bfloat16, device=dev)
@@ -427,7 +430,7 @@ def bench_layer(args, torch, kda):
     work = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     def parts(i, sp):
-        w1, w2 = w_ins[i % copies], w_os[i % copies]
+        w1, w2 = w_ins[i % in_copies], w_os[i % o_copies]
         return [
             lambda: lib.kda_in_proj(xs.data_ptr(), HIDDEN, w1.data_ptr(), projected.data_ptr(),
                                     pitch, S, HIDDEN, H, work.data_ptr(), ws_bytes, sp),
@@ -462,7 +465,8 @@ def bench_layer(args, torch, kda):
         b.record(stream)
         torch.cuda.synchronize()
         alone[name] = round(a.elapsed_time(b) / steps * 1e3, 2)
-    # one HIP graph holding `copies` whole steps (every weight copy once)
+    # one HIP graph holding `copies` whole steps (every in_proj weight copy once)
+    copies = in_copies
     graph = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
@@ -487,7 +491,7 @@ def bench_layer(args, torch, kda):
     return {"workload": case.name, "rows": S, "heads": H, "hidden": HIDDEN,
             "eager_us_per_step": round(eager_us, 2), "graph_us_per_step": round(graph_us, 2),
             "tokens_per_s_graph": round(S / (graph_us * 1e-6), 1),
-            "kernel_us_alone": alone, "weight_copies_rotated": copies,
+            "kernel_us_alone": alone, "weight_copies_rotated": {"in_proj": in_copies, "o_proj": o_copies},
             "note": "synthetic weights; the core's inputs are in_proj's outputs"}
 
 
