@@ -9,7 +9,7 @@
 //   docstring and stage_o: o_proj over the core rows (K = 1536 local), an
 //   MFMA GEMV with the token dimension padded to 16.
 //
-// Three GEMM kernels, chosen by the row count M and K, and a slice sum:
+// Four GEMM kernels, chosen by the row count M and K, and a slice sum:
 //
 // Skinny (M <= 16 when K is a multiple of 64 but not of 128, up to 64 rows
 // when K is not a multiple of 64): both operands are K-contiguous (rows of X,
@@ -28,8 +28,8 @@
 // over 4 slices of workgroups and linear_split_sum adds the fp32 slices in
 // slice order. Pipelined (above 256 rows, K >= 4096, tiles filling three
 // quarters to all but one of the CUs): the same tiles and arithmetic with the
-// fragment reads overlapping the MFMAs and the idle CUs prefetching the tiles'
-// lines into L2. Tiled (M > 64, other K): 128 x 64 tiles staged through
+// fragment reads overlapping the MFMAs and the idle CUs loading the tiles' W
+// lines ahead of them. Tiled (M > 64, other K): 128 x 64 tiles staged through
 // registers.
 #include "kda_internal.h"
 
