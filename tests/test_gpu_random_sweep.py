@@ -40,7 +40,7 @@ def _core_params(i):
                 a_log_range=[(-1.0, 1.0), (-3.0, 2.0)][int(rng.integers(0, 2))])
 
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(48))
 def test_core_random_combination(i):
     from gpu_cases import run_gpu
     prm = _core_params(i)
@@ -74,7 +74,7 @@ def _linear_params(i):
                 y_extra=int(rng.integers(0, 5)), workspace=bool(rng.integers(0, 2)) or i % 3 == 2)
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(48))
 def test_linear_random_shape(i):
     import kimi_delta_attention_conv_amd as kda
     import oracle
